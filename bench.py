@@ -1,0 +1,272 @@
+"""Benchmark of the fp32 matrix product on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--shape M,N,K] [--algo NAME]
+
+One step is one call of sgemm_f32 (the whole product) on inputs already resident
+in HBM.  The default workload is C = A·B with M = N = K = 8192 and N(0,1) inputs
+(the compute-bound point); the 2048 x 3072 x 4096 product (A 2048 x 4096, B 4096 x
+3072) is timed after it and reported under "also".  Rank 0 prints one JSON line.
+
+Throughput is 2MNK / t (page "CUDA算子优化(4)：矩阵乘法", section "计算强度": 2K flops
+per output element); the algorithmic byte count is 4(MK + KN + MN) (same section),
+used for the intensity I = MNK / (2(MK + KN + MN)).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (matrix and vector), 2.4 GHz
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_mfma_8192_traffic.txt")
+KERNEL_SOURCES = ["dense_fp32_matrix_f32_amd/csrc/mfma.hip",
+                  "dense_fp32_matrix_f32_amd/csrc/tile_order.h",
+                  "dense_fp32_matrix_f32_amd/csrc/internal.h"]
+
+
+def algorithmic_flops(M: int, N: int, K: int) -> int:
+    """2MNK: K multiplies and K adds per output element."""
+    return 2 * M * N * K
+
+
+def algorithmic_bytes(M: int, N: int, K: int) -> int:
+    """4(MK + KN + MN): read A and B once, write C once, in fp32."""
+    return 4 * (M * K + K * N + M * N)
+
+
+def intensity(M: int, N: int, K: int) -> float:
+    """Flops per byte, MNK / (2(MK + KN + MN)); N/6 for a square product."""
+    return algorithmic_flops(M, N, K) / algorithmic_bytes(M, N, K)
+
+
+def naive_global_reads(n: int) -> int:
+    """Element reads of the one-thread-per-output kernel on an n x n product: 2n^3."""
+    return 2 * n ** 3
+
+
+def tiled_global_reads(n: int, tile: int) -> int:
+    """Element reads of the tiled kernel: every loaded element serves `tile` outputs."""
+    return 2 * n ** 3 // tile
+
+
+def tile_intensity(tm: int, tn: int) -> float:
+    """Flops per byte of one tm x tn tile step (page "CUDA算子优化(4)：矩阵乘法",
+    section "版本V1共享内存分块"): 2*tm*tn*tk / ((tm*tk + tn*tk)*4)."""
+    return 2 * tm * tn / ((tm + tn) * 4)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
+    on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE, encoding="utf-8") as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def host_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def make_inputs(torch, M, N, K, seed):
+    import synthgen
+    A = synthgen.matrix(M, K, seed=seed, stream=0, dist="normal")
+    B = synthgen.matrix(K, N, seed=seed, stream=1, dist="normal")
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    return A, B, dA, dB, dC
+
+
+def time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warmup):
+    """Warm-up, then `steps` timed launches: wall clock between two full
+    synchronisations, and per-launch HIP events on the launch stream."""
+    stream = torch.cuda.current_stream()
+    lda, ldb, ldc = K, N, N
+
+    def call():
+        st = sg.sgemm_f32_algo(M, N, K, dA.data_ptr(), lda, dB.data_ptr(), ldb, dC.data_ptr(), ldc,
+                               stream.cuda_stream, algo)
+        if st != 0:
+            raise sg.SgemmError(st)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, kernel_ms
+
+
+def cpu_baseline(A, B, M, N, K, budget_s: float):
+    """Time the oracle on whole rows of C until about `budget_s` of CPU time is spent."""
+    import numpy as np
+
+    import oracle
+    threads = host_threads()
+    row_cost = N * K
+    # calibrate with one row per thread
+    rows = threads
+    r = np.repeat(np.arange(rows) * (M // max(rows, 1)), N)
+    c = np.tile(np.arange(N), rows)
+    t0 = time.perf_counter()
+    oracle.sgemm_elems(A[:, :K], B[:, :N], r, c, threads=threads)
+    t1 = time.perf_counter() - t0
+    per_row = t1 / rows
+    more = max(0, int((budget_s - t1) / max(per_row, 1e-9)))
+    more = min(more, M - rows)
+    if more > 0:
+        r2 = np.repeat(np.linspace(0, M - 1, more).astype(np.int64), N)
+        c2 = np.tile(np.arange(N), more)
+        t0 = time.perf_counter()
+        oracle.sgemm_elems(A[:, :K], B[:, :N], r2, c2, threads=threads)
+        t2 = time.perf_counter() - t0
+        rows_total, secs = rows + more, t1 + t2
+    else:
+        rows_total, secs = rows, t1
+    flops = 2.0 * rows_total * row_cost
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_total} whole rows of C ({rows_total}x{N} outputs, {K}-term fp64 sums) "
+                      f"of the {M}x{N}x{K} product in {secs:.1f} s"}
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--shape", default="8192,8192,8192", help="M,N,K of the timed product")
+    p.add_argument("--algo", default="auto")
+    p.add_argument("--seed", type=int, default=6)
+    p.add_argument("--no-also", action="store_true", help="skip the 2048x3072x4096 product")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="CPU time budget of the oracle baseline (0 = skip)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a device copy of known size (for HBM counter calibration)")
+    args = p.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import dense_fp32_matrix_f32_amd as sg
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    sg.lib()
+
+    if args.copy_calibration:
+        n = 64 << 20  # 64 Mi floats = 256 MiB each way
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 3}), flush=True)
+        return
+
+    M, N, K = (int(x) for x in args.shape.split(","))
+    algo = sg.ALGOS[args.algo]
+    print(f"[bench] generating {M}x{K} and {K}x{N} N(0,1) inputs (seed {args.seed})",
+          file=sys.stderr, flush=True)
+    A, B, dA, dB, dC = make_inputs(torch, M, N, K, args.seed)
+    chosen = sg.sgemm_f32_select(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N)
+    used = chosen if algo == sg.ALGO_AUTO else algo
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up, algo "
+          f"{sg.sgemm_f32_algo_name(used)}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall, kms = time_product(torch, sg, M, N, K, dA, dB, dC, algo, args.steps, args.warmup)
+    flops = algorithmic_flops(M, N, K)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (wall / args.steps) / 1e12
+    kavg = sum(kms) / len(kms)
+    achieved = flops / (kavg * 1e-3) / 1e12
+    rec = {
+        "metric": "SGEMM TFLOP/s (2MNK/t) + % FP32 peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_fp32_peak": round(100 * value / PEAK_FP32_TFLOPS, 2),
+        "config": {"workload": f"C=A*B fp32 row-major M={M} N={N} K={K}, A,B iid N(0,1) "
+                               f"seed {args.seed}",
+                   "M": M, "N": N, "K": K, "algo": sg.sgemm_f32_algo_name(used),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                     "traffic": read_traffic() if (M, N, K) == (8192, 8192, 8192) else None,
+                     "kernel_ms_avg": round(kavg, 4), "kernel_ms_min": round(min(kms), 4),
+                     "algorithmic_flops": flops, "algorithmic_bytes": algorithmic_bytes(M, N, K),
+                     "intensity_flop_per_byte": round(intensity(M, N, K), 2)},
+    }
+    del dA, dB, dC
+    if not args.no_also:
+        m2, n2, k2 = 2048, 3072, 4096
+        print(f"[bench] timing {m2}x{n2}x{k2}", file=sys.stderr, flush=True)
+        _, _, eA, eB, eC = make_inputs(torch, m2, n2, k2, 3)
+        w2, k2ms = time_product(torch, sg, m2, n2, k2, eA, eB, eC, sg.ALGO_AUTO, args.steps,
+                                args.warmup)
+        f2 = algorithmic_flops(m2, n2, k2)
+        k2avg = sum(k2ms) / len(k2ms)
+        rec["also"] = {"workload": f"C=A*B fp32 row-major M={m2} N={n2} K={k2}, N(0,1) seed 3",
+                       "value": round(f2 / (w2 / args.steps) / 1e12, 3), "unit": "TFLOP/s",
+                       "kernel_tflops": round(f2 / (k2avg * 1e-3) / 1e12, 3),
+                       "kernel_ms_avg": round(k2avg, 4),
+                       "pct_fp32_peak": round(100 * f2 / (k2avg * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 2)}
+        del eA, eB, eC
+    if args.cpu_seconds > 0:
+        print(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr,
+              flush=True)
+        rec["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

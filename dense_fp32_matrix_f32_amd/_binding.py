@@ -1,0 +1,85 @@
+"""ctypes binding of include/sgemm_f32.h: the same entry points, same arguments.
+
+This layer only marshals arguments.  Every step of the product runs in the HIP
+kernels of libsgemm_f32.so; there is no fallback of any kind, and a missing
+library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsgemm_f32.so")
+
+ALGO_AUTO = 0
+ALGO_NAIVE = 1
+ALGO_LDS_TILED = 2
+ALGO_VALU_REGBLOCK = 3
+ALGO_MFMA = 4
+ALGO_SKINNY = 5
+ALGO_COUNT = 6
+ALGOS = {"auto": ALGO_AUTO, "naive": ALGO_NAIVE, "lds_tiled": ALGO_LDS_TILED,
+         "valu_regblock": ALGO_VALU_REGBLOCK, "mfma": ALGO_MFMA, "skinny": ALGO_SKINNY}
+
+HIP_SUCCESS = 0
+HIP_ERROR_INVALID_VALUE = 1
+
+EXPORTED = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name")
+
+_lib = None
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, what: str = "sgemm_f32"):
+        super().__init__(f"{what} returned hipError_t {status}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        # torch ships its own HIP runtime under the same soname as ROCm's.  Load it
+        # first so that this library binds to it: one runtime per process, which is
+        # what makes torch's device pointers and stream handles valid here.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(hipcc, gfx950); there is no other implementation")
+        l = ctypes.CDLL(LIB_PATH)
+        i, vp = ctypes.c_int, ctypes.c_void_p
+        args = [i, i, i, vp, i, vp, i, vp, i, vp]
+        l.sgemm_f32.argtypes = args
+        l.sgemm_f32.restype = i
+        l.sgemm_f32_algo.argtypes = args + [i]
+        l.sgemm_f32_algo.restype = i
+        l.sgemm_f32_select.argtypes = [i, i, i, vp, i, vp, i, vp, i]
+        l.sgemm_f32_select.restype = i
+        l.sgemm_f32_algo_name.argtypes = [i]
+        l.sgemm_f32_algo_name.restype = ctypes.c_char_p
+        _lib = l
+    return _lib
+
+
+def sgemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    """C = A·B; pointers are device addresses (int); returns the hipError_t."""
+    return lib().sgemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def sgemm_f32_algo(M, N, K, A, lda, B, ldb, C, ldc, stream=0, algo=ALGO_AUTO) -> int:
+    """As sgemm_f32 with a forced algorithm id; returns the hipError_t."""
+    return lib().sgemm_f32_algo(M, N, K, A, lda, B, ldb, C, ldc, stream, algo)
+
+
+def sgemm_f32_select(M, N, K, A, lda, B, ldb, C, ldc) -> int:
+    """Algorithm id AUTO would use (host-only), or -1 for invalid arguments."""
+    return lib().sgemm_f32_select(M, N, K, A, lda, B, ldb, C, ldc)
+
+
+def sgemm_f32_algo_name(algo: int) -> str:
+    return lib().sgemm_f32_algo_name(algo).decode()

@@ -1,0 +1,102 @@
+// basic.hip -- the first two rungs of the kernel ladder and the empty-sum fill.
+//
+// Rung 0 (naive) and rung 1 (LDS-tiled) are the two GPU designs that the pages
+// build: one thread per output element reading A and B straight from global
+// memory, then the same mapping with A and B staged tile by tile in on-chip
+// memory.  They are kept as reference points for the faster rungs and accept
+// every shape.
+#include "internal.h"
+
+namespace sgemm {
+
+// ---------------------------------------------------------------------------
+// K == 0: every C[i][j] is the empty sum, 0.
+__global__ __launch_bounds__(256) void zero_fill_kernel(int M, int N, float *__restrict__ C,
+                                                        int64_t ldc) {
+    const int64_t total = (int64_t)M * N;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+        const int64_t i = e / N, j = e - i * N;
+        C[i * ldc + j] = 0.0f;
+    }
+}
+
+hipError_t launch_zero_fill(const Problem &p, hipStream_t s) {
+    const int64_t total = (int64_t)p.M * p.N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    return launch(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.M, p.N, p.C, p.ldc);
+}
+
+// ---------------------------------------------------------------------------
+// Rung 0: one work-item per element of C, the sum over k read directly from
+// global memory (page "CUDA内存优化入门：从Naive到Tiled矩阵乘法—Week2学习总结", §五;
+// page "CUDA算子优化(4)：矩阵乘法", section "版本V1朴素矩阵乘法").
+// A 64 x 4 work-group puts one wave on 64 consecutive columns of one row, so the
+// reads of B and the store of C are contiguous across the wave and A[i][k] is a
+// single address per wave.
+constexpr int NAIVE_X = 64, NAIVE_Y = 4;
+
+__global__ __launch_bounds__(NAIVE_X *NAIVE_Y) void naive_kernel(
+    int M, int N, int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
+    int64_t ldb, float *__restrict__ C, int64_t ldc, int tiles_n) {
+    const int bn = blockIdx.x % tiles_n, bm = blockIdx.x / tiles_n;
+    const int col = bn * NAIVE_X + threadIdx.x;
+    const int row = bm * NAIVE_Y + threadIdx.y;
+    if (row >= M || col >= N) return;
+    const float *a = A + (int64_t)row * lda;
+    const float *b = B + col;
+    float sum = 0.0f;
+    for (int k = 0; k < K; ++k) sum = fmaf(a[k], b[(int64_t)k * ldb], sum);
+    C[(int64_t)row * ldc + col] = sum;
+}
+
+hipError_t launch_naive(const Problem &p, hipStream_t s) {
+    const int64_t tiles_n = (p.N + NAIVE_X - 1) / NAIVE_X;
+    const int64_t tiles_m = (p.M + NAIVE_Y - 1) / NAIVE_Y;
+    if (tiles_n * tiles_m > INT32_MAX) return hipErrorInvalidValue;
+    return launch(naive_kernel, dim3((unsigned)(tiles_n * tiles_m)), dim3(NAIVE_X, NAIVE_Y), 0, s,
+                  p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, (int)tiles_n);
+}
+
+// ---------------------------------------------------------------------------
+// Rung 1: 16 x 16 output tile per work-group, A and B staged through LDS one
+// 16 x 16 tile at a time (page "CUDA内存优化入门：从Naive到Tiled矩阵乘法—Week2学习总结",
+// §六; page "【infra之路】Tiled Matrix Multiplication详解").  Partial tiles at the
+// M, N and K edges are filled with zeros (§六, handling of sizes that are not a
+// multiple of the tile), and there are two barriers per step: after the tile is
+// written (before it is read) and after it is read (before it is overwritten).
+// Rows are padded to 17 floats (§八, bank-conflict padding) so that the
+// column-wise reads of the B tile fall in distinct banks.
+constexpr int TILE = 16;
+
+__global__ __launch_bounds__(TILE *TILE) void lds_tiled_kernel(
+    int M, int N, int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
+    int64_t ldb, float *__restrict__ C, int64_t ldc, int tiles_n) {
+    __shared__ float As[TILE][TILE + 1];
+    __shared__ float Bs[TILE][TILE + 1];
+    const int tx = threadIdx.x, ty = threadIdx.y;
+    const int bn = blockIdx.x % tiles_n, bm = blockIdx.x / tiles_n;
+    const int row = bm * TILE + ty, col = bn * TILE + tx;
+    float sum = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += TILE) {
+        const int ka = k0 + tx, kb = k0 + ty;
+        As[ty][tx] = (row < M && ka < K) ? A[(int64_t)row * lda + ka] : 0.0f;
+        Bs[ty][tx] = (kb < K && col < N) ? B[(int64_t)kb * ldb + col] : 0.0f;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TILE; ++k) sum = fmaf(As[ty][k], Bs[k][tx], sum);
+        __syncthreads();
+    }
+    if (row < M && col < N) C[(int64_t)row * ldc + col] = sum;
+}
+
+hipError_t launch_lds_tiled(const Problem &p, hipStream_t s) {
+    const int64_t tiles_n = (p.N + TILE - 1) / TILE;
+    const int64_t tiles_m = (p.M + TILE - 1) / TILE;
+    if (tiles_n * tiles_m > INT32_MAX) return hipErrorInvalidValue;
+    return launch(lds_tiled_kernel, dim3((unsigned)(tiles_n * tiles_m)), dim3(TILE, TILE), 0, s,
+                  p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, (int)tiles_n);
+}
+
+}  // namespace sgemm

@@ -1,0 +1,136 @@
+// skinny.hip -- products with very few rows (M <= 8), e.g. a 1 x K row times K x N.
+//
+// With M = 1 the intensity formula of the page "CUDA算子优化(4)：矩阵乘法" (section
+// "计算强度", I = MNK / (2(MK + KN + MN))) gives about 0.5 flop per byte, far below
+// the chip's ridge point: the product is bound by reading B once from HBM.  The
+// kernel therefore streams B exactly once with 16-byte loads, keeps up to 8 rows
+// of A in flight per element of B, and splits K across the 256 work-items of a
+// work-group (k = slot, slot + S, slot + 2S, ...), followed by a fixed-order
+// reduction in LDS, so results are reproducible and no atomics are needed.
+#include "internal.h"
+
+namespace sgemm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int SKINNY_THREADS = 256;
+constexpr int SKINNY_MAX_ROWS = 8;
+
+__device__ __forceinline__ f32x4 load16_skinny(const float *p) {
+    f32x4 v;
+    __builtin_memcpy(&v, p, 16);
+    return v;
+}
+
+// LPR work-items share one row segment of 4*LPR columns; S = 256/LPR k slots.
+template <int MR, int LPR>
+__global__ __launch_bounds__(SKINNY_THREADS) void skinny_kernel(
+    int M, int N, int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
+    int64_t ldb, float *__restrict__ C, int64_t ldc) {
+    constexpr int CW = 4 * LPR;               // columns per work-group
+    constexpr int S = SKINNY_THREADS / LPR;   // k slots
+    constexpr int U = 8;                      // independent loads in flight per work-item
+    __shared__ float red[S][MR * CW + 1];
+
+    const int tid = threadIdx.x;
+    const int q = tid % LPR, slot = tid / LPR;
+    const int n0 = blockIdx.x * CW;
+    const int n = n0 + 4 * q;
+    const bool vec = n + 3 < N;
+
+    const float *arow[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) arow[m] = A + (int64_t)min(m, M - 1) * lda;
+
+    float acc[MR][4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m][0] = acc[m][1] = acc[m][2] = acc[m][3] = 0.0f;
+
+    auto load_b = [&](int k) -> f32x4 {
+        const float *row = B + (int64_t)k * ldb;
+        if (vec) return load16_skinny(row + n);
+        f32x4 v;
+        v.x = row[min(n + 0, N - 1)];
+        v.y = row[min(n + 1, N - 1)];
+        v.z = row[min(n + 2, N - 1)];
+        v.w = row[min(n + 3, N - 1)];
+        return v;
+    };
+
+    int k = slot;
+    for (; k + (U - 1) * S < K; k += U * S) {
+        f32x4 b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[u] = load_b(k + u * S);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float a = arow[m][k + u * S];
+                acc[m][0] = fmaf(a, b[u].x, acc[m][0]);
+                acc[m][1] = fmaf(a, b[u].y, acc[m][1]);
+                acc[m][2] = fmaf(a, b[u].z, acc[m][2]);
+                acc[m][3] = fmaf(a, b[u].w, acc[m][3]);
+            }
+        }
+    }
+    for (; k < K; k += S) {
+        const f32x4 b = load_b(k);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const float a = arow[m][k];
+            acc[m][0] = fmaf(a, b.x, acc[m][0]);
+            acc[m][1] = fmaf(a, b.y, acc[m][1]);
+            acc[m][2] = fmaf(a, b.z, acc[m][2]);
+            acc[m][3] = fmaf(a, b.w, acc[m][3]);
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[slot][m * CW + 4 * q + e] = acc[m][e];
+    __syncthreads();
+
+    // Fixed-order sum over the k slots: one work-item per (row, column).
+    for (int o = tid; o < MR * CW; o += SKINNY_THREADS) {
+        const int m = o / CW, c = o % CW;
+        float sum = 0.0f;
+        for (int t = 0; t < S; ++t) sum += red[t][o];
+        if (m < M && n0 + c < N) C[(int64_t)m * ldc + n0 + c] = sum;
+    }
+}
+
+template <int MR>
+static hipError_t launch_rows(const Problem &p, hipStream_t s) {
+    // Wide segments give longer contiguous row reads; narrow ones give more
+    // work-groups.  Keep at least 256 work-groups (one per CU) when N allows.
+    if (p.N >= 64 * 256) {
+        const int64_t groups = (p.N + 63) / 64;
+        return launch(skinny_kernel<MR, 16>, dim3((unsigned)groups), dim3(SKINNY_THREADS), 0, s,
+                      p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
+    }
+    const int64_t groups = (p.N + 15) / 16;
+    return launch(skinny_kernel<MR, 4>, dim3((unsigned)groups), dim3(SKINNY_THREADS), 0, s, p.M,
+                  p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
+}
+
+hipError_t launch_skinny(const Problem &p, hipStream_t s) {
+    if ((int64_t)(p.N + 15) / 16 > INT32_MAX) return hipErrorInvalidValue;
+    // More than 8 rows: one pass per group of 8 rows.
+    for (int r0 = 0; r0 < p.M; r0 += SKINNY_MAX_ROWS) {
+        Problem q = p;
+        q.M = p.M - r0 < SKINNY_MAX_ROWS ? p.M - r0 : SKINNY_MAX_ROWS;
+        q.A = p.A + (int64_t)r0 * p.lda;
+        q.C = p.C + (int64_t)r0 * p.ldc;
+        hipError_t e;
+        if (q.M == 1) e = launch_rows<1>(q, s);
+        else if (q.M == 2) e = launch_rows<2>(q, s);
+        else if (q.M <= 4) e = launch_rows<4>(q, s);
+        else e = launch_rows<8>(q, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace sgemm

@@ -1,0 +1,105 @@
+/*
+ * sgemm_f32.h -- single-precision matrix product C = A·B on one MI355X (gfx950).
+ *
+ * The operation.  For A (M x K), B (K x N) and C (M x N),
+ *     C[i][j] = sum over k = 0 .. K-1 of A[i][k] * B[k][j]
+ * as defined on the page "CUDA算子优化(4)：矩阵乘法" (section "矩阵乘法的数学定义")
+ * and on the page "CUDA内存优化入门：从Naive到Tiled矩阵乘法—Week2学习总结" (§三,
+ * "数学公式").  This is alpha = 1, beta = 0: C is overwritten and never read.
+ *
+ * Layout.  All three matrices are row-major in device memory with element
+ * strides (leading dimensions): A[i][k] = A[i*lda + k], B[k][j] = B[k*ldb + j],
+ * C[i][j] = C[i*ldc + j].  The pages store dense rows (ld equal to the row
+ * length); larger leading dimensions address sub-matrices and padded rows,
+ * whose padding is never read or written.
+ *
+ * Arithmetic.  Products and sums are IEEE fp32 with round-to-nearest-even;
+ * multiply-adds are fused.  The summation order over k is not specified
+ * beyond this: any order is a correct result of the definition (its error is
+ * bounded by K * 2^-24 * sum_k |A[i][k]| * |B[k][j]|).  For a fixed shape,
+ * leading dimensions and algorithm, results are bitwise reproducible run to
+ * run (no atomics).  NaN and Inf propagate as IEEE arithmetic dictates.
+ *
+ * Ownership.  The caller owns every buffer.  A, B and C are device pointers
+ * (hipMalloc, torch or any other device allocation) that must stay valid
+ * until the enqueued work completes.  The library allocates nothing, keeps
+ * no pointer after returning, and holds no mutable global state; calls may
+ * come from several host threads.
+ *
+ * Asynchrony.  Each call validates its arguments on the host, enqueues its
+ * kernels on `stream` (0 is the null stream) and returns without waiting.
+ * The caller synchronises (hipStreamSynchronize, events, ...).
+ *
+ * Errors (returned, never fatal; nothing is enqueued on an error):
+ *   hipErrorInvalidValue   M, N or K negative; lda < max(1,K); ldb < max(1,N);
+ *                          ldc < max(1,N); A or B NULL when M*N*K > 0; C NULL
+ *                          when M*N > 0; the written extent of C overlapping
+ *                          the read extent of A or B; unknown algorithm id;
+ *                          a launch grid beyond the device's limits.
+ *   otherwise              the status of the launch (for example
+ *                          hipErrorNoDevice on a host without a GPU).
+ * Empty cases: M == 0 or N == 0 returns hipSuccess and enqueues nothing.
+ * K == 0 writes C[i][j] = 0 (the empty sum) for i < M, j < N.
+ */
+#ifndef SGEMM_F32_H
+#define SGEMM_F32_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Algorithm ids for sgemm_f32_algo(). */
+#define SGEMM_F32_ALGO_AUTO 0          /* chosen from shape and alignment */
+#define SGEMM_F32_ALGO_NAIVE 1         /* one thread per element of C */
+#define SGEMM_F32_ALGO_LDS_TILED 2     /* 16x16 tiles staged in LDS */
+#define SGEMM_F32_ALGO_VALU_REGBLOCK 3 /* LDS double buffer, 8x8 register tiles, v_fma_f32 */
+#define SGEMM_F32_ALGO_MFMA 4          /* LDS double buffer, fp32 matrix cores */
+#define SGEMM_F32_ALGO_SKINNY 5        /* M <= 8: stream B once, split K in the work-group */
+#define SGEMM_F32_ALGO_COUNT 6
+
+/*
+ * C = A·B with the algorithm chosen for the shape (SGEMM_F32_ALGO_AUTO).
+ *   M, N, K      rows of A and C, columns of B and C, columns of A / rows of B.
+ *   A, lda       device pointer to A (M x K), row stride lda elements.
+ *   B, ldb       device pointer to B (K x N), row stride ldb elements.
+ *   C, ldc       device pointer to C (M x N), row stride ldc elements; written only.
+ *   stream       HIP stream the work is enqueued on.
+ * Returns hipSuccess once the work is enqueued, or an error as listed above.
+ */
+hipError_t sgemm_f32(int M, int N, int K,
+                     const float *A, int lda,
+                     const float *B, int ldb,
+                     float *C, int ldc,
+                     hipStream_t stream);
+
+/*
+ * Same operation and contract as sgemm_f32(), forcing one algorithm of the
+ * ladder (an SGEMM_F32_ALGO_* id).  Every algorithm accepts every valid
+ * shape; SGEMM_F32_ALGO_SKINNY with M > 8 processes the rows in groups of 8.
+ */
+hipError_t sgemm_f32_algo(int M, int N, int K,
+                          const float *A, int lda,
+                          const float *B, int ldb,
+                          float *C, int ldc,
+                          hipStream_t stream, int algo);
+
+/*
+ * The algorithm SGEMM_F32_ALGO_AUTO picks for these arguments (host-only:
+ * no HIP call is made).  Returns an SGEMM_F32_ALGO_* id other than AUTO, or
+ * -1 if the arguments are invalid.
+ */
+int sgemm_f32_select(int M, int N, int K,
+                     const float *A, int lda,
+                     const float *B, int ldb,
+                     const float *C, int ldc);
+
+/* Static, NUL-terminated name of an algorithm id ("invalid" if unknown). */
+const char *sgemm_f32_algo_name(int algo);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_F32_H */

@@ -1,0 +1,116 @@
+"""Host-side checks of the C-ABI library: exports, argument validation, dispatch
+choice and the work-group -> tile mapping.  No kernel is launched."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import dense_fp32_matrix_f32_amd as sg
+from dense_fp32_matrix_f32_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID = _binding.HIP_ERROR_INVALID_VALUE
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M):
+            if not m.group(0).startswith("#"):
+                names.add(m.group(1))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert {"sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name"} <= declared
+    lib = ctypes.CDLL(sg.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+    assert set(_binding.EXPORTED) == declared
+
+
+def test_algo_names():
+    assert [sg.sgemm_f32_algo_name(i) for i in range(sg.ALGO_COUNT)] == list(sg.ALGOS)
+    assert sg.sgemm_f32_algo_name(99) == "invalid"
+    assert sg.sgemm_f32_algo_name(-1) == "invalid"
+
+
+# Fake, well-separated "device" addresses: validation only looks at the numbers.
+A_ADDR, B_ADDR, C_ADDR = 1 << 32, 2 << 32, 3 << 32
+
+
+@pytest.mark.parametrize("args", [
+    dict(M=-1), dict(N=-1), dict(K=-1),
+    dict(lda=7), dict(ldb=15), dict(ldc=15),          # ld below the row length
+    dict(A=0), dict(B=0), dict(C=0),                  # null operands of a non-empty product
+    dict(C=A_ADDR + 4 * 10),                          # C inside A
+    dict(B=C_ADDR + 4 * 100),                         # B inside C
+])
+def test_invalid_arguments_rejected_before_any_hip_call(args):
+    base = dict(M=8, N=16, K=8, A=A_ADDR, lda=8, B=B_ADDR, ldb=16, C=C_ADDR, ldc=16)
+    base.update(args)
+    for algo in range(sg.ALGO_COUNT):
+        st = sg.sgemm_f32_algo(base["M"], base["N"], base["K"], base["A"], base["lda"],
+                               base["B"], base["ldb"], base["C"], base["ldc"], 0, algo)
+        assert st == INVALID, (args, algo, st)
+    assert sg.sgemm_f32_select(base["M"], base["N"], base["K"], base["A"], base["lda"],
+                               base["B"], base["ldb"], base["C"], base["ldc"]) == -1
+
+
+def test_unknown_algorithm_rejected():
+    assert sg.sgemm_f32_algo(8, 8, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR, 8, 0, 17) == INVALID
+    assert sg.sgemm_f32_algo(8, 8, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR, 8, 0, -1) == INVALID
+
+
+def test_empty_products_succeed_without_launch():
+    # M == 0 or N == 0: nothing to do, even with null pointers
+    assert sg.sgemm_f32(0, 16, 8, 0, 8, 0, 16, 0, 16, 0) == 0
+    assert sg.sgemm_f32(8, 0, 8, 0, 8, 0, 1, 0, 1, 0) == 0
+    # K == 0 with null A/B is valid (C is zero-filled): validation passes
+    assert sg.sgemm_f32_select(8, 16, 0, 0, 1, 0, 16, C_ADDR, 16) > 0
+
+
+def test_selection():
+    assert sg.sgemm_f32_select(1, 4096, 4096, A_ADDR, 4096, B_ADDR, 4096, C_ADDR, 4096) == \
+        sg.ALGO_SKINNY
+    assert sg.sgemm_f32_select(8192, 8192, 8192, A_ADDR, 8192, B_ADDR, 8192, C_ADDR, 8192) == \
+        sg.ALGO_MFMA
+    assert sg.sgemm_f32_select(4095, 4097, 1023, A_ADDR, 1023, B_ADDR, 4097, C_ADDR, 4097) == \
+        sg.ALGO_MFMA
+
+
+def test_no_device_is_an_error_not_a_crash():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    a = np.zeros(64, np.float32)
+    b = np.zeros(64, np.float32)
+    c = np.zeros(64, np.float32)
+    st = sg.sgemm_f32(8, 8, 8, a.ctypes.data, 8, b.ctypes.data, 8, c.ctypes.data, 8, 0)
+    assert st not in (0, INVALID)
+
+
+def test_tile_order_is_a_bijection(tmp_path):
+    exe = tmp_path / "tile_order_check"
+    subprocess.check_call(["g++", "-O1", "-std=c++17",
+                           "-I", os.path.join(ROOT, "dense_fp32_matrix_f32_amd", "csrc"),
+                           os.path.join(ROOT, "tests", "host", "tile_order_check.cpp"),
+                           "-o", str(exe)])
+    shapes = []
+    for tm in (1, 2, 3, 7, 8, 9, 16, 33, 64):
+        for tn in (1, 5, 8, 12, 13, 32, 33):
+            for g in (1, 4, 8):
+                shapes += [tm, tn, g]
+    shapes += [32, 33, 8, 64, 32, 8, 16, 16, 8]   # the ragged and 8192^3 grids
+    out = subprocess.run([str(exe), *map(str, shapes)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout[-2000:]
