@@ -410,22 +410,35 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(
     // the block and column TN*lr + j of the wave's strip ----
     const bool full = (m0 + T::BM <= M) && (n0 + T::BN <= N);
     const int col0 = n0 + wn * T::WN + T::TN * lr;
+    const int row0 = m0 + wm * T::WM + 4 * lh;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i) {
+        for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * T::WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            float *dst = C + (int64_t)row * ldc + col0;
-            if (full) {
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + i * 32 + 8 * (r >> 2) + (r & 3);
                 float v[T::TN];
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j) v[j] = acc[i][j][r];
-                __builtin_memcpy(dst, v, sizeof(v));
-            } else if (row < M) {
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-                    if (col0 + j < N) dst[j] = acc[i][j][r];
+                __builtin_memcpy(C + (int64_t)row * ldc + col0, v, sizeof(v));
             }
+            // one row block at a time keeps few accumulators in flight
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + i * 32 + 8 * (r >> 2) + (r & 3);
+                if (row < M) {
+                    float *dst = C + (int64_t)row * ldc + col0;
+#pragma unroll
+                    for (int j = 0; j < T::TN; ++j)
+                        if (col0 + j < N) dst[j] = acc[i][j][r];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
