@@ -168,6 +168,31 @@ def cpu_baseline(A, B, M, N, K, budget_s: float):
                       f"of the {M}x{N}x{K} product in {secs:.1f} s"}
 
 
+def ladder(torch, sg, M, N, K, args):
+    """Kernel time of each algorithm on one product (warm-up by time, as above)."""
+    _, _, dA, dB, dC = make_inputs(torch, M, N, K, args.seed)
+    flops = algorithmic_flops(M, N, K)
+    nbytes = algorithmic_bytes(M, N, K)
+    for name, algo in sg.ALGOS.items():
+        if algo == sg.ALGO_AUTO:
+            continue
+        # one probe launch sizes the warm-up and the timed count
+        _, probe = time_product(torch, sg, M, N, K, dA, dB, dC, algo, 1, 1)
+        est = max(probe[0], 1e-3)
+        warm = max(args.warmup, min(2000, int(300 / est)))
+        steps = max(args.steps, min(2000, int(200 / est)))
+        _, kms = time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warm)
+        avg = sum(kms) / len(kms)
+        print(json.dumps({"shape": [M, N, K], "algo": name, "kernel_ms_avg": round(avg, 5),
+                          "tflops": round(flops / (avg * 1e-3) / 1e12, 3),
+                          "pct_fp32_peak": round(100 * flops / (avg * 1e-3) / 1e12 /
+                                                 PEAK_FP32_TFLOPS, 2),
+                          "gbs": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                          "pct_hbm_peak": round(100 * nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                2),
+                          "steps": steps, "warmup": warm}), flush=True)
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -181,6 +206,9 @@ def main(argv=None):
                    help="CPU time budget of the oracle baseline (0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a device copy of known size (for HBM counter calibration)")
+    p.add_argument("--ladder", action="store_true",
+                   help="time every algorithm of the ladder on --shape instead (one JSON line "
+                        "per algorithm)")
     args = p.parse_args(argv)
 
     if args.gpus != 1:
@@ -207,6 +235,9 @@ def main(argv=None):
         return
 
     M, N, K = (int(x) for x in args.shape.split(","))
+    if args.ladder:
+        ladder(torch, sg, M, N, K, args)
+        return
     algo = sg.ALGOS[args.algo]
     print(f"[bench] generating {M}x{K} and {K}x{N} N(0,1) inputs (seed {args.seed})",
           file=sys.stderr, flush=True)

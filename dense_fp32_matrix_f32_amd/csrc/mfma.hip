@@ -101,7 +101,7 @@ __device__ __forceinline__ void interleave() {
 }
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int KW_, int GROUP_M_, int STAGES_ = 2,
-          int OCC_ = 1>
+          int OCC_ = 1, int PAD_A_ = 4, int PAD_B_ = 8>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, KW = KW_;
     static constexpr int GROUP_M = GROUP_M_, STAGES = STAGES_, OCC = OCC_;
@@ -110,8 +110,8 @@ struct MfmaTile {
     static constexpr int THREADS = SPATIAL * KW * 64;
     static constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 accumulators per wave
     static constexpr int ACC = TM * TN * 16;             // accumulator floats per lane
-    static constexpr int PA = BK + 4;                    // A row pitch in LDS (floats)
-    static constexpr int PB = BN + 8;                    // B row pitch in LDS (floats)
+    static constexpr int PA = BK + PAD_A_;               // A row pitch in LDS (floats)
+    static constexpr int PB = BN + PAD_B_;               // B row pitch in LDS (floats)
     static constexpr int A_STAGE = BM * PA, B_STAGE = BK * PB;
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int RED = (KW - 1) * SPATIAL * 64 * ACC;  // split-k partials
@@ -128,21 +128,38 @@ struct MfmaTile {
     static_assert(TN == 1 || TN == 2 || TN == 4, "a lane holds 1, 2 or 4 adjacent columns");
     static_assert(BK % (8 * KW) == 0 && BK % 4 == 0, "k window splits into 8-wide steps");
     static_assert(THREADS <= 1024, "work-group size");
+    static_assert(PAD_A_ % 4 == 0 && PAD_B_ % 4 == 0, "16-byte aligned LDS rows");
     static_assert(STAGES == 2 || (STAGES == 3 && STEPS % 2 == 0),
                   "a three-stage ring carries fragments across windows in an even step count");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 };
 
-template <class T>
-__global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(
-    int M, int N, int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
-    int64_t ldb, float *__restrict__ C, int64_t ldc, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) float lds[T::LDS_FLOATS];
-    typedef typename VecOf<T::TN>::type BVec;
+// The operands of one product.
+struct GemmArgs {
+    int M, N, K;
+    const float *__restrict__ A;
+    int64_t lda;
+    const float *__restrict__ B;
+    int64_t ldb;
+    float *__restrict__ C;
+    int64_t ldc;
+};
 
-    int tm, tn;
-    tile_order(blockIdx.x, tiles_m, tiles_n, T::GROUP_M, &tm, &tn);
-    const int m0 = tm * T::BM, n0 = tn * T::BN;
+template <class T>
+using Acc = f32x16[T::TM][T::TN];
+
+// acc += the product of A rows m0..m0+BM-1 and B columns n0..n0+BN-1 over the
+// k windows [w_begin, w_end) (window w covers k = w*BK .. w*BK+BK-1).  Called by
+// every work-item of the group; uses all of `lds` and ends on a barrier, so LDS
+// is free again when it returns.
+template <class T>
+__device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, int n0,
+                                         int w_begin, int w_end, Acc<T> &acc) {
+    typedef typename VecOf<T::TN>::type BVec;
+    const int M = g.M, N = g.N, K = g.K;
+    const int64_t lda = g.lda, ldb = g.ldb;
+    const float *__restrict__ A = g.A;
+    const float *__restrict__ B = g.B;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, lh = lane >> 5;
@@ -249,12 +266,6 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(
             if (has_b(v)) *(f32x4 *)(s + b_lds[v]) = rb[v];
     };
 
-    f32x16 acc[T::TM][T::TN];
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) acc[i][j] = f32x16{};
-
     const int a_frag = (wm * T::WM + lr) * T::PA + 4 * lh;
     const int b_frag = T::A_STAGE + (4 * lh) * T::PB + wn * T::WN + T::TN * lr;
 
@@ -282,22 +293,21 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(
                         f.a[i][q], lane_of<T::TN>(f.b[q], j), acc[i][j], 0, 0, 0);
     };
 
-    const int windows = (K + T::BK - 1) / T::BK;
     // Prologue: the first STAGES-1 windows go to LDS, the next one to registers.
-    fetch(0);
+    fetch(w_begin * T::BK);
     stash(0);
     if constexpr (T::STAGES == 3) {
-        if (windows > 1) {
-            fetch(T::BK);
+        if (w_begin + 1 < w_end) {
+            fetch((w_begin + 1) * T::BK);
             stash(1);
         }
     }
     __syncthreads();
-    if (windows > T::STAGES - 1) fetch((T::STAGES - 1) * T::BK);
+    if (w_begin + T::STAGES - 1 < w_end) fetch((w_begin + T::STAGES - 1) * T::BK);
 
     Frag frag[2];
     int cur = 0;  // LDS stage of window w
-    int w = 0;
+    int w = w_begin;
     if constexpr (T::STAGES == 3) read_frag(frag[0], lds, 0);
 
     // Steady state: a work-group whose columns lie inside B, on a window whose
@@ -307,7 +317,7 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(
     // spread one by one between the MFMAs of the first step instead of
     // stalling the matrix cores in a block of their own.
     if (cols_inside) {
-        const int steady_end = K / T::BK - T::STAGES;
+        const int steady_end = min(w_end, K / T::BK) - T::STAGES;
         for (; w < steady_end; ++w) {
             const float *s = lds + cur * T::STAGE;
             const int next = cur + 1 == T::STAGES ? 0 : cur + 1;
@@ -348,7 +358,7 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(
 
     // Remaining windows (the last STAGES ones, a partial last window, work-groups
     // on the right edge of C): the same schedule with the copies guarded.
-    for (; w < windows; ++w) {
+    for (; w < w_end; ++w) {
         const float *s = lds + cur * T::STAGE;
         const int next = cur + 1 == T::STAGES ? 0 : cur + 1;
         if constexpr (T::STAGES == 2) read_frag(frag[0], s, 0);
@@ -368,46 +378,28 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(
         }
         // Window w + STAGES - 1 goes from registers to the stage freed by window w - 1,
         // and the loads of the window after it are issued.
-        if (w + T::STAGES - 1 < windows) {
+        if (w + T::STAGES - 1 < w_end) {
             const int fill = cur == 0 ? T::STAGES - 1 : cur - 1;
             stash(fill);
-            if (w + T::STAGES < windows) fetch((w + T::STAGES) * T::BK);
+            if (w + T::STAGES < w_end) fetch((w + T::STAGES) * T::BK);
         }
         __syncthreads();
         cur = next;
     }
+}
 
-    // ---- split-k: groups 1..KW-1 hand their partial blocks to group 0 ----
-    if constexpr (T::KW > 1) {
-        float *red = lds + sw * 64 * T::ACC + lane;
-        constexpr int GROUP_STRIDE = T::SPATIAL * 64 * T::ACC;
-        if (kg > 0) {
-            float *dst = red + (kg - 1) * GROUP_STRIDE;
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dst[((i * T::TN + j) * 16 + r) * 64] = acc[i][j][r];
-        }
-        __syncthreads();
-        if (kg > 0) return;
-#pragma unroll
-        for (int g = 1; g < T::KW; ++g) {
-            const float *src = red + (g - 1) * GROUP_STRIDE;
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[i][j][r] += src[((i * T::TN + j) * 16 + r) * 64];
-        }
-    }
-
-    // ---- epilogue: accumulator r of block (i, j) holds row 8*(r/4) + 4*lh + r%4 of
-    // the block and column TN*lr + j of the wave's strip ----
+// Store the accumulators of block (m0, n0) to C; rows >= M and columns >= N are
+// skipped.  Accumulator r of block (i, j) holds row 8*(r/4) + 4*lh + r%4 of the
+// block and column TN*lr + j of the wave's strip.
+template <class T>
+__device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, const Acc<T> &acc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int sw = wave % T::SPATIAL;
+    const int wm = sw / T::WAVES_N, wn = sw % T::WAVES_N;
+    const int M = g.M, N = g.N;
+    float *__restrict__ C = g.C;
+    const int64_t ldc = g.ldc;
     const bool full = (m0 + T::BM <= M) && (n0 + T::BN <= N);
     const int col0 = n0 + wn * T::WN + T::TN * lr;
     const int row0 = m0 + wm * T::WM + 4 * lh;
@@ -443,28 +435,96 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(
     }
 }
 
+// Split-k inside the work-group: groups 1..KW-1 hand their partial blocks to
+// group 0 through LDS, which adds them in group order.  Returns true for the
+// waves that hold the finished block.
+template <class T>
+__device__ __forceinline__ bool kw_reduce(float *lds, Acc<T> &acc) {
+    if constexpr (T::KW == 1) {
+        return true;
+    } else {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int kg = wave / T::SPATIAL, sw = wave % T::SPATIAL;
+        float *red = lds + sw * 64 * T::ACC + lane;
+        constexpr int GROUP_STRIDE = T::SPATIAL * 64 * T::ACC;
+        if (kg > 0) {
+            float *dst = red + (kg - 1) * GROUP_STRIDE;
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dst[((i * T::TN + j) * 16 + r) * 64] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (kg > 0) return false;
+#pragma unroll
+        for (int gi = 1; gi < T::KW; ++gi) {
+            const float *src = red + (gi - 1) * GROUP_STRIDE;
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[i][j][r] += src[((i * T::TN + j) * 16 + r) * 64];
+        }
+        return true;
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void zero_acc(Acc<T> &acc) {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) acc[i][j] = f32x16{};
+}
+
+// Data-parallel form: one work-group per BM x BN block of C.
+template <class T>
+__global__ __launch_bounds__(T::THREADS, T::OCC) void mfma_kernel(GemmArgs g, int tiles_m,
+                                                                 int tiles_n) {
+    __shared__ __attribute__((aligned(16))) float lds[T::LDS_FLOATS];
+    int tm, tn;
+    tile_order(blockIdx.x, tiles_m, tiles_n, T::GROUP_M, &tm, &tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    Acc<T> acc;
+    zero_acc<T>(acc);
+    mma_tile<T>(g, lds, m0, n0, 0, (g.K + T::BK - 1) / T::BK, acc);
+    if (!kw_reduce<T>(lds, acc)) return;
+    store_tile<T>(g, m0, n0, acc);
+}
+
 template <class T>
 static hipError_t launch_tile(const Problem &p, hipStream_t s) {
     const int64_t tiles_m = (p.M + T::BM - 1) / T::BM;
     const int64_t tiles_n = (p.N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > INT32_MAX) return hipErrorInvalidValue;
-    return launch(mfma_kernel<T>, dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0, s,
-                  p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, (int)tiles_m, (int)tiles_n);
+    const GemmArgs g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc};
+    return launch(mfma_kernel<T>, dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0, s, g,
+                  (int)tiles_m, (int)tiles_n);
 }
 
 // ---------------------------------------------------------------------------
 // Tile choice.  A launch of T tiles on U compute units finishes when the busiest
 // CU has worked through ceil(T / U) tiles, so a configuration's time is modelled
-// as ceil(T / U) * 2*BM*BN*K / (e / U) + t0: e is the throughput (TFLOP/s over the
-// whole chip) the configuration sustains when every CU is busy and t0 its fixed
-// cost per launch (ramp-up, prologue, epilogue).  Both were fitted to
-// measurements of every configuration on the 512^3, 1024^3, 2048 x 3072 x 4096,
-// 4095 x 4097 x 1023 and 8192^3 products on MI355X.  The smallest estimate wins.
+// as ceil(T / U) * 2*BM*BN*K / (e / 256) + t0, where e is a whole-chip throughput
+// in TFLOP/s and t0 a fixed cost per launch (ramp-up, prologue, epilogue).  Each
+// configuration has two throughputs: one for products whose A and B together
+// fit in 200 MB (inside the 256 MB Infinity Cache), one for larger products.
+// All three numbers per configuration were fitted to timings of every
+// configuration on 15 shapes on MI355X (the 512^3, 1024^3, 2048 x 3072 x 4096,
+// 4095 x 4097 x 1023 and 8192^3 products among them); on each of those shapes
+// the model picks the fastest measured configuration.  The smallest estimate
+// wins.
 struct TileChoice {
     hipError_t (*launch)(const Problem &, hipStream_t);
     int bm, bn;
-    double tflops;  // e
-    double t0_us;   // t0
+    double tflops_cached;  // e, A and B within 200 MB
+    double tflops_large;   // e, larger A and B
+    double t0_us;          // t0
 };
 
 // 256 x 256 blocks, one wave per SIMD with 128 x 128 of C each: large products.
@@ -482,15 +542,15 @@ using TileSplit64x4 = MfmaTile<64, 64, 32, 32, 64, 4, 4, 2>;
 using TileTiny = MfmaTile<32, 32, 32, 32, 32, 4, 4, 2>;
 
 static const TileChoice kTiles[] = {
-    {launch_tile<TileHuge>, 256, 256, 139.5, 6.5},
-    {launch_tile<TileLarge>, 256, 128, 134.5, 3.5},
-    {launch_tile<TileWide>, 128, 128, 134.0, 5.5},
-    {launch_tile<TileSplit192>, 128, 192, 125.5, 14.5},
-    {launch_tile<TileMid>, 64, 128, 125.5, 9.0},
-    {launch_tile<TileSmall>, 64, 64, 120.0, 9.0},
-    {launch_tile<TileSplit64>, 64, 64, 117.5, 7.5},
-    {launch_tile<TileSplit64x4>, 64, 64, 98.5, 5.5},
-    {launch_tile<TileTiny>, 32, 32, 101.5, 7.0},
+    {launch_tile<TileHuge>, 256, 256, 132.0, 150.0, 11.0},
+    {launch_tile<TileLarge>, 256, 128, 123.0, 145.0, 7.0},
+    {launch_tile<TileWide>, 128, 128, 123.0, 139.0, 4.0},
+    {launch_tile<TileSplit192>, 128, 192, 119.0, 104.0, 18.0},
+    {launch_tile<TileMid>, 64, 128, 112.0, 109.0, 8.0},
+    {launch_tile<TileSmall>, 64, 64, 115.0, 120.0, 9.0},
+    {launch_tile<TileSplit64>, 64, 64, 115.0, 127.0, 6.0},
+    {launch_tile<TileSplit64x4>, 64, 64, 110.0, 123.0, 7.0},
+    {launch_tile<TileTiny>, 32, 32, 99.0, 105.0, 7.0},
 };
 
 static int compute_units() {
@@ -510,7 +570,9 @@ static int choose_tile(int M, int N, int K, int cus) {
         const TileChoice &c = kTiles[i];
         const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         const double per_cu = std::ceil(tiles / cus);
-        const double per_cu_tflops = c.tflops / 256.0;  // fitted on 256 CUs
+        const double operands = 4.0 * ((double)M * K + (double)K * N);
+        const double per_cu_tflops =
+            (operands <= 200e6 ? c.tflops_cached : c.tflops_large) / 256.0;  // fitted on 256 CUs
         const double us = per_cu * 2.0 * c.bm * c.bn * (double)K / (per_cu_tflops * 1e6) + c.t0_us;
         if (i == 0 || us < best_us) {
             best = i;

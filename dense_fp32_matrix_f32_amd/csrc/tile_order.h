@@ -12,17 +12,19 @@ namespace sgemm {
 
 // Work-groups of one launch are handed to the 8 XCDs of the chip round-robin
 // (work-group id p runs on XCD p % 8), and each XCD has its own L2.  This maps
-// the hardware order to a logical tile order in which every XCD owns one
-// contiguous run of logical ids, and walks the logical ids in groups of
-// `group_m` tile-rows so that the tiles resident on one XCD at a time share
-// rows of A and columns of B.  The map is a bijection on [0, tiles_m*tiles_n).
-SGEMM_HD inline void tile_order(int pid, int tiles_m, int tiles_n, int group_m,
-                                int *tm, int *tn) {
-    const int nwg = tiles_m * tiles_n;
+// hardware id p of a launch of n work-groups to a virtual id such that every
+// XCD owns one contiguous run of virtual ids.  A bijection on [0, n).
+SGEMM_HD inline int xcd_remap(int pid, int n) {
     const int xcd = pid & 7, slot = pid >> 3;
-    const int per = nwg >> 3, rem = nwg & 7;
-    const int logical = xcd < rem ? xcd * (per + 1) + slot
-                                  : rem * (per + 1) + (xcd - rem) * per + slot;
+    const int per = n >> 3, rem = n & 7;
+    return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// Virtual tile index -> (tile row, tile column), walking `group_m` tile-rows at
+// a time so that consecutive indices share rows of A and columns of B.  A
+// bijection from [0, tiles_m*tiles_n) onto the tile grid.
+SGEMM_HD inline void group_tile(int logical, int tiles_m, int tiles_n, int group_m, int *tm,
+                                int *tn) {
     const int group = group_m * tiles_n;
     const int g = logical / group;
     const int first_m = g * group_m;
@@ -30,6 +32,13 @@ SGEMM_HD inline void tile_order(int pid, int tiles_m, int tiles_n, int group_m,
     const int in_group = logical - g * group;
     *tm = first_m + in_group % rows;
     *tn = in_group / rows;
+}
+
+// One work-group per tile: the tiles resident on one XCD at a time form compact
+// groups of C.  A bijection from [0, tiles_m*tiles_n) onto the tile grid.
+SGEMM_HD inline void tile_order(int pid, int tiles_m, int tiles_n, int group_m, int *tm,
+                                int *tn) {
+    group_tile(xcd_remap(pid, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 }  // namespace sgemm
