@@ -4,16 +4,17 @@
 // "计算强度", I = MNK / (2(MK + KN + MN))) gives about 0.5 flop per byte, far below
 // the chip's ridge point: the product is bound by reading B once from HBM.  The
 // kernel therefore streams B exactly once with 16-byte loads, keeps up to 8 rows
-// of A in flight per element of B, and splits K across the 256 work-items of a
+// of A in flight per element of B, and splits K across the work-items of a
 // work-group (k = slot, slot + S, slot + 2S, ...), followed by a fixed-order
-// reduction in LDS, so results are reproducible and no atomics are needed.
+// pairwise reduction in LDS, so results are reproducible and no atomics are
+// needed.  Up to 1024 work-items per group keep enough 16-byte loads in flight
+// per CU to cover HBM latency.
 #include "internal.h"
 
 namespace sgemm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int SKINNY_THREADS = 256;
 constexpr int SKINNY_MAX_ROWS = 8;
 
 __device__ __forceinline__ f32x4 load16_skinny(const float *p) {
@@ -22,15 +23,18 @@ __device__ __forceinline__ f32x4 load16_skinny(const float *p) {
     return v;
 }
 
-// LPR work-items share one row segment of 4*LPR columns; S = 256/LPR k slots.
-template <int MR, int LPR>
-__global__ __launch_bounds__(SKINNY_THREADS) void skinny_kernel(
+// THREADS work-items; LPR of them share one row segment of 4*LPR columns, so
+// there are S = THREADS/LPR k slots.  MR is the number of rows of A handled.
+template <int MR, int LPR, int THREADS>
+__global__ __launch_bounds__(THREADS) void skinny_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
     int64_t ldb, float *__restrict__ C, int64_t ldc) {
-    constexpr int CW = 4 * LPR;               // columns per work-group
-    constexpr int S = SKINNY_THREADS / LPR;   // k slots
-    constexpr int U = 8;                      // independent loads in flight per work-item
-    __shared__ float red[S][MR * CW + 1];
+    constexpr int CW = 4 * LPR;        // columns per work-group
+    constexpr int S = THREADS / LPR;   // k slots (a power of two)
+    constexpr int OUT = MR * CW;       // outputs per work-group
+    constexpr int U = 8;               // independent loads in flight per work-item
+    static_assert((S & (S - 1)) == 0, "slot count is a power of two");
+    __shared__ float red[S][OUT + 1];
 
     const int tid = threadIdx.x;
     const int q = tid % LPR, slot = tid / LPR;
@@ -56,26 +60,7 @@ __global__ __launch_bounds__(SKINNY_THREADS) void skinny_kernel(
         v.w = row[min(n + 3, N - 1)];
         return v;
     };
-
-    int k = slot;
-    for (; k + (U - 1) * S < K; k += U * S) {
-        f32x4 b[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) b[u] = load_b(k + u * S);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                const float a = arow[m][k + u * S];
-                acc[m][0] = fmaf(a, b[u].x, acc[m][0]);
-                acc[m][1] = fmaf(a, b[u].y, acc[m][1]);
-                acc[m][2] = fmaf(a, b[u].z, acc[m][2]);
-                acc[m][3] = fmaf(a, b[u].w, acc[m][3]);
-            }
-        }
-    }
-    for (; k < K; k += S) {
-        const f32x4 b = load_b(k);
+    auto fma4 = [&](int k, const f32x4 &b) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             const float a = arow[m][k];
@@ -84,7 +69,17 @@ __global__ __launch_bounds__(SKINNY_THREADS) void skinny_kernel(
             acc[m][2] = fmaf(a, b.z, acc[m][2]);
             acc[m][3] = fmaf(a, b.w, acc[m][3]);
         }
+    };
+
+    int k = slot;
+    for (; k + (U - 1) * S < K; k += U * S) {
+        f32x4 b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[u] = load_b(k + u * S);
+#pragma unroll
+        for (int u = 0; u < U; ++u) fma4(k + u * S, b[u]);
     }
+    for (; k < K; k += S) fma4(k, load_b(k));
 
 #pragma unroll
     for (int m = 0; m < MR; ++m)
@@ -92,26 +87,32 @@ __global__ __launch_bounds__(SKINNY_THREADS) void skinny_kernel(
         for (int e = 0; e < 4; ++e) red[slot][m * CW + 4 * q + e] = acc[m][e];
     __syncthreads();
 
-    // Fixed-order sum over the k slots: one work-item per (row, column).
-    for (int o = tid; o < MR * CW; o += SKINNY_THREADS) {
+    // Fixed pairwise tree over the k slots: slot s absorbs slot s + stride.
+#pragma unroll
+    for (int stride = S / 2; stride > 0; stride >>= 1) {
+        for (int e = tid; e < stride * OUT; e += THREADS) {
+            const int sl = e / OUT, o = e - sl * OUT;
+            red[sl][o] += red[sl + stride][o];
+        }
+        __syncthreads();
+    }
+    for (int o = tid; o < OUT; o += THREADS) {
         const int m = o / CW, c = o % CW;
-        float sum = 0.0f;
-        for (int t = 0; t < S; ++t) sum += red[t][o];
-        if (m < M && n0 + c < N) C[(int64_t)m * ldc + n0 + c] = sum;
+        if (m < M && n0 + c < N) C[(int64_t)m * ldc + n0 + c] = red[0][o];
     }
 }
 
-template <int MR>
+template <int MR, int THREADS>
 static hipError_t launch_rows(const Problem &p, hipStream_t s) {
     // Wide segments give longer contiguous row reads; narrow ones give more
     // work-groups.  Keep at least 256 work-groups (one per CU) when N allows.
     if (p.N >= 64 * 256) {
         const int64_t groups = (p.N + 63) / 64;
-        return launch(skinny_kernel<MR, 16>, dim3((unsigned)groups), dim3(SKINNY_THREADS), 0, s,
+        return launch(skinny_kernel<MR, 16, THREADS>, dim3((unsigned)groups), dim3(THREADS), 0, s,
                       p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
     }
     const int64_t groups = (p.N + 15) / 16;
-    return launch(skinny_kernel<MR, 4>, dim3((unsigned)groups), dim3(SKINNY_THREADS), 0, s, p.M,
+    return launch(skinny_kernel<MR, 4, THREADS>, dim3((unsigned)groups), dim3(THREADS), 0, s, p.M,
                   p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
 }
 
@@ -124,10 +125,11 @@ hipError_t launch_skinny(const Problem &p, hipStream_t s) {
         q.A = p.A + (int64_t)r0 * p.lda;
         q.C = p.C + (int64_t)r0 * p.ldc;
         hipError_t e;
-        if (q.M == 1) e = launch_rows<1>(q, s);
-        else if (q.M == 2) e = launch_rows<2>(q, s);
-        else if (q.M <= 4) e = launch_rows<4>(q, s);
-        else e = launch_rows<8>(q, s);
+        // Fewer rows leave room for more work-items (loads in flight) per group.
+        if (q.M == 1) e = launch_rows<1, 1024>(q, s);
+        else if (q.M == 2) e = launch_rows<2, 512>(q, s);
+        else if (q.M <= 4) e = launch_rows<4, 512>(q, s);
+        else e = launch_rows<8, 256>(q, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
