@@ -18,9 +18,11 @@ ALGO_LDS_TILED = 2
 ALGO_VALU_REGBLOCK = 3
 ALGO_MFMA = 4
 ALGO_SKINNY = 5
-ALGO_COUNT = 6
+ALGO_SKINNY_N = 6
+ALGO_COUNT = 7
 ALGOS = {"auto": ALGO_AUTO, "naive": ALGO_NAIVE, "lds_tiled": ALGO_LDS_TILED,
-         "valu_regblock": ALGO_VALU_REGBLOCK, "mfma": ALGO_MFMA, "skinny": ALGO_SKINNY}
+         "valu_regblock": ALGO_VALU_REGBLOCK, "mfma": ALGO_MFMA, "skinny": ALGO_SKINNY,
+         "skinny_n": ALGO_SKINNY_N}
 
 HIP_SUCCESS = 0
 HIP_ERROR_INVALID_VALUE = 1

@@ -39,5 +39,6 @@ hipError_t launch_lds_tiled(const Problem &p, hipStream_t s);
 hipError_t launch_valu_regblock(const Problem &p, hipStream_t s);
 hipError_t launch_mfma(const Problem &p, hipStream_t s);
 hipError_t launch_skinny(const Problem &p, hipStream_t s);
+hipError_t launch_skinny_n(const Problem &p, hipStream_t s);
 
 }  // namespace sgemm

@@ -36,10 +36,12 @@ hipError_t validate(int M, int N, int K, const float *A, int lda, const float *B
     return hipSuccess;
 }
 
+// Few rows or few columns: the product streams one operand and is bound by
+// memory, so the streaming kernels win; everything else goes to matrix cores.
 int choose(int M, int N, int K) {
-    (void)N;
     (void)K;
     if (M <= 8) return SGEMM_F32_ALGO_SKINNY;
+    if (N <= 8) return SGEMM_F32_ALGO_SKINNY_N;
     return SGEMM_F32_ALGO_MFMA;
 }
 
@@ -53,6 +55,7 @@ extern "C" const char *sgemm_f32_algo_name(int algo) {
     case SGEMM_F32_ALGO_VALU_REGBLOCK: return "valu_regblock";
     case SGEMM_F32_ALGO_MFMA: return "mfma";
     case SGEMM_F32_ALGO_SKINNY: return "skinny";
+    case SGEMM_F32_ALGO_SKINNY_N: return "skinny_n";
     default: return "invalid";
     }
 }
@@ -79,6 +82,7 @@ extern "C" hipError_t sgemm_f32_algo(int M, int N, int K, const float *A, int ld
     case SGEMM_F32_ALGO_VALU_REGBLOCK: return sgemm::launch_valu_regblock(p, stream);
     case SGEMM_F32_ALGO_MFMA: return sgemm::launch_mfma(p, stream);
     case SGEMM_F32_ALGO_SKINNY: return sgemm::launch_skinny(p, stream);
+    case SGEMM_F32_ALGO_SKINNY_N: return sgemm::launch_skinny_n(p, stream);
     default: return hipErrorInvalidValue;
     }
 }

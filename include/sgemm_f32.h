@@ -51,13 +51,14 @@ extern "C" {
 #endif
 
 /* Algorithm ids for sgemm_f32_algo(). */
-#define SGEMM_F32_ALGO_AUTO 0          /* chosen from shape and alignment */
+#define SGEMM_F32_ALGO_AUTO 0          /* chosen from the shape */
 #define SGEMM_F32_ALGO_NAIVE 1         /* one thread per element of C */
 #define SGEMM_F32_ALGO_LDS_TILED 2     /* 16x16 tiles staged in LDS */
 #define SGEMM_F32_ALGO_VALU_REGBLOCK 3 /* LDS double buffer, 8x8 register tiles, v_fma_f32 */
 #define SGEMM_F32_ALGO_MFMA 4          /* LDS double buffer, fp32 matrix cores */
 #define SGEMM_F32_ALGO_SKINNY 5        /* M <= 8: stream B once, split K in the work-group */
-#define SGEMM_F32_ALGO_COUNT 6
+#define SGEMM_F32_ALGO_SKINNY_N 6      /* N <= 8: stream A once, split K across a wave */
+#define SGEMM_F32_ALGO_COUNT 7
 
 /*
  * C = A·B with the algorithm chosen for the shape (SGEMM_F32_ALGO_AUTO).
@@ -77,7 +78,8 @@ hipError_t sgemm_f32(int M, int N, int K,
 /*
  * Same operation and contract as sgemm_f32(), forcing one algorithm of the
  * ladder (an SGEMM_F32_ALGO_* id).  Every algorithm accepts every valid
- * shape; SGEMM_F32_ALGO_SKINNY with M > 8 processes the rows in groups of 8.
+ * shape; SGEMM_F32_ALGO_SKINNY with M > 8 processes the rows in groups of 8,
+ * SGEMM_F32_ALGO_SKINNY_N with N > 8 the columns in groups of 8.
  */
 hipError_t sgemm_f32_algo(int M, int N, int K,
                           const float *A, int lda,

@@ -84,6 +84,12 @@ def test_selection():
         sg.ALGO_MFMA
     assert sg.sgemm_f32_select(4095, 4097, 1023, A_ADDR, 1023, B_ADDR, 4097, C_ADDR, 4097) == \
         sg.ALGO_MFMA
+    assert sg.sgemm_f32_select(4096, 1, 4096, A_ADDR, 4096, B_ADDR, 1, C_ADDR, 1) == \
+        sg.ALGO_SKINNY_N
+    assert sg.sgemm_f32_select(4096, 8, 4096, A_ADDR, 4096, B_ADDR, 8, C_ADDR, 8) == \
+        sg.ALGO_SKINNY_N
+    assert sg.sgemm_f32_select(8, 8, 4096, A_ADDR, 4096, B_ADDR, 8, C_ADDR, 8) == \
+        sg.ALGO_SKINNY
 
 
 def test_no_device_is_an_error_not_a_crash():

@@ -22,7 +22,7 @@ from gpu_helpers import (Device, assert_close, assert_guards, check_full, check_
 pytestmark = pytest.mark.gpu
 
 LADDER = [sg.ALGO_NAIVE, sg.ALGO_LDS_TILED, sg.ALGO_VALU_REGBLOCK, sg.ALGO_MFMA, sg.ALGO_SKINNY,
-          sg.ALGO_AUTO]
+          sg.ALGO_SKINNY_N, sg.ALGO_AUTO]
 FAST = [sg.ALGO_VALU_REGBLOCK, sg.ALGO_MFMA, sg.ALGO_AUTO]
 name = sg.sgemm_f32_algo_name
 
@@ -204,7 +204,7 @@ def test_nan_stays_in_its_row_and_column(algo):
     assert not np.any(np.isfinite(np.delete(C[:, 101], 17)))
 
 
-@pytest.mark.parametrize("algo", FAST + [sg.ALGO_SKINNY], ids=name)
+@pytest.mark.parametrize("algo", FAST + [sg.ALGO_SKINNY, sg.ALGO_SKINNY_N], ids=name)
 def test_bitwise_reproducible(algo):
     M, N, K = 1000, 1100, 700
     A, B = inputs(M, N, K, "normal", seed=11)
@@ -241,3 +241,63 @@ def test_torch_matmul_helper():
     torch.cuda.synchronize()
     check_full(np.ascontiguousarray(A[:, :100]), np.ascontiguousarray(B[:100]), 333, 444, 100,
                C2.cpu().numpy(), "view")
+
+
+# ---------------------------------------------------------------- few columns
+FEW_COLS = [(4096, 1, 4096), (4095, 3, 1023), (1000, 8, 777), (33, 5, 4099), (4096, 9, 257),
+            (17, 2, 1), (300, 7, 5)]
+
+
+@pytest.mark.parametrize("algo", [sg.ALGO_SKINNY_N, sg.ALGO_AUTO], ids=name)
+@pytest.mark.parametrize("shape", FEW_COLS, ids=lambda s: "x".join(map(str, s)))
+def test_few_columns(shape, algo):
+    M, N, K = shape
+    A, B = inputs(M, N, K, "smallint", seed=300 + M + N + K)
+    C = _run(A, B, M, N, K, algo)
+    check_full(A, B, M, N, K, C, f"{name(algo)} {shape} int", exact=True)
+    A, B = inputs(M, N, K, "normal", seed=400 + M + N + K, lda=K + 1)
+    C = _run(A, B, M, N, K, algo, offset_elems=1)
+    check_full(A, B, M, N, K, C, f"{name(algo)} {shape}")
+
+
+# ---------------------------------------------------------------- 64-bit offsets
+def _big_case(M, N, K, algo, rows=None, cols=None):
+    """An operand of more than 2^31 elements, drawn on the device (seeded); the
+    oracle checks whole sampled rows and columns of C from host copies of the
+    rows of A and columns of B they need."""
+    torch = torch_cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    dA = torch.empty((M, K), device="cuda").uniform_(-1, 1, generator=gen)
+    dB = torch.empty((K, N), device="cuda").uniform_(-1, 1, generator=gen)
+    dC = torch.full((M, N), float("nan"), device="cuda")
+    log(f"[gpu] 64-bit offsets {name(algo)} M={M} N={N} K={K}")
+    st = sg.sgemm_f32_algo(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N,
+                           torch.cuda.current_stream().cuda_stream, algo)
+    assert st == 0
+    torch.cuda.synchronize()
+    rows = rows if rows is not None else [0, 1, M // 2, M - 2, M - 1]
+    cols = cols if cols is not None else [0, 1, N // 2, N - 2, N - 1]
+    rows = sorted(set(r for r in rows if 0 <= r < M))
+    cols = sorted(set(c for c in cols if 0 <= c < N))
+    Bh = dB[:, cols].cpu().numpy()
+    Ar = dA[rows].cpu().numpy()
+    Cref, S = oracle.sgemm(np.ascontiguousarray(Ar), np.ascontiguousarray(Bh))
+    Cg = dC[rows][:, cols].cpu().numpy()
+    assert_close(Cg, Cref, S, f"{name(algo)} rows x cols beyond 2^31 elements")
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+
+
+def test_offsets_beyond_2_31_mfma():
+    # A: 131073 x 16387 = 2.148e9 elements; its last rows start past 2^31.
+    _big_case(131073, 40, 16387, sg.ALGO_AUTO)
+
+
+def test_offsets_beyond_2_31_few_columns():
+    _big_case(131073, 3, 16387, sg.ALGO_SKINNY_N)
+
+
+def test_offsets_beyond_2_31_few_rows():
+    # B: 65537 x 32769 = 2.148e9 elements; its last rows start past 2^31.
+    _big_case(3, 32769, 65537, sg.ALGO_SKINNY)
