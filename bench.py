@@ -193,6 +193,56 @@ def ladder(torch, sg, M, N, K, args):
                           "steps": steps, "warmup": warm}), flush=True)
 
 
+# Shapes of the tile-choice model: the five workloads and nine others that mix
+# wave quantisation, ragged edges, short and long k, and cached and uncached sizes.
+TILE_SHAPES = [(8192, 8192, 8192), (2048, 3072, 4096), (4095, 4097, 1023), (1024, 1024, 1024),
+               (512, 512, 512), (3000, 2000, 1500), (1000, 5000, 2000), (6000, 6000, 1000),
+               (256, 8192, 8192), (8192, 256, 8192), (4096, 4096, 256), (16384, 16384, 1024),
+               (2048, 2048, 2048), (4096, 4096, 4096), (128, 128, 65536)]
+
+
+def tile_sweep(torch, sg, shapes, args):
+    """Kernel time of every tile configuration of the matrix-core rung on each shape
+    (one JSON line per shape and configuration)."""
+    stream = torch.cuda.current_stream()
+    for (M, N, K) in shapes:
+        _, _, dA, dB, dC = make_inputs(torch, M, N, K, args.seed)
+        flops = algorithmic_flops(M, N, K)
+
+        def launch(tile):
+            st = sg.sgemm_f32_mfma_tile(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N,
+                                        dC.data_ptr(), N, stream.cuda_stream, tile)
+            if st != 0:
+                raise sg.SgemmError(st, "sgemm_f32_mfma_tile")
+
+        def timed(tile, n):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(n)]
+            for a, b in ev:
+                a.record(stream)
+                launch(tile)
+                b.record(stream)
+            torch.cuda.synchronize()
+            return [a.elapsed_time(b) for a, b in ev]
+
+        auto = sg.sgemm_f32_mfma_select(M, N, K, torch.cuda.get_device_properties(0)
+                                        .multi_processor_count)
+        # clocks settle on about half a second of work before the first timing
+        est = max(timed(auto, 2)[-1], 1e-3)
+        timed(auto, max(1, min(5000, int(500 / est))))
+        for tile in range(sg.sgemm_f32_mfma_tiles()):
+            est = max(min(timed(tile, 2)), 1e-3)
+            timed(tile, max(2, min(2000, int(50 / est))))
+            kms = timed(tile, max(args.steps, min(2000, int(150 / est))))
+            avg = sum(kms) / len(kms)
+            print(json.dumps({"shape": [M, N, K], "tile": tile,
+                              "name": sg.sgemm_f32_mfma_tile_name(tile), "chosen": tile == auto,
+                              "kernel_ms_avg": round(avg, 5), "kernel_ms_min": round(min(kms), 5),
+                              "tflops": round(flops / (avg * 1e-3) / 1e12, 2), "steps": len(kms)}),
+                  flush=True)
+        del dA, dB, dC
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -209,6 +259,9 @@ def main(argv=None):
     p.add_argument("--ladder", action="store_true",
                    help="time every algorithm of the ladder on --shape instead (one JSON line "
                         "per algorithm)")
+    p.add_argument("--tiles", action="store_true",
+                   help="time every tile configuration of the matrix-core rung on --shape, or on "
+                        "the tile-model shapes with --shape all (one JSON line per configuration)")
     args = p.parse_args(argv)
 
     if args.gpus != 1:
@@ -234,6 +287,11 @@ def main(argv=None):
         print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 3}), flush=True)
         return
 
+    if args.tiles:
+        shapes = TILE_SHAPES if args.shape == "all" else \
+            [tuple(int(x) for x in args.shape.split(","))]
+        tile_sweep(torch, sg, shapes, args)
+        return
     M, N, K = (int(x) for x in args.shape.split(","))
     if args.ladder:
         ladder(torch, sg, M, N, K, args)

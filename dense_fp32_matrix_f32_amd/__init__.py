@@ -10,10 +10,12 @@ from __future__ import annotations
 from ._binding import (ALGO_AUTO, ALGO_COUNT, ALGO_LDS_TILED, ALGO_MFMA, ALGO_NAIVE,
                        ALGO_SKINNY, ALGO_SKINNY_N, ALGO_VALU_REGBLOCK, ALGOS, EXPORTED, LIB_PATH,
                        SgemmError, lib, sgemm_f32, sgemm_f32_algo, sgemm_f32_algo_name,
-                       sgemm_f32_select)
+                       sgemm_f32_mfma_select, sgemm_f32_mfma_tile, sgemm_f32_mfma_tile_name,
+                       sgemm_f32_mfma_tiles, sgemm_f32_select)
 
 __all__ = ["matmul", "sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name",
-           "SgemmError", "ALGOS", "LIB_PATH", "EXPORTED", "lib"]
+           "sgemm_f32_mfma_tiles", "sgemm_f32_mfma_tile_name", "sgemm_f32_mfma_select",
+           "sgemm_f32_mfma_tile", "SgemmError", "ALGOS", "LIB_PATH", "EXPORTED", "lib"]
 
 
 def _operand(t, name):

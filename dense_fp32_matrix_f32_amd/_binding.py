@@ -27,7 +27,9 @@ ALGOS = {"auto": ALGO_AUTO, "naive": ALGO_NAIVE, "lds_tiled": ALGO_LDS_TILED,
 HIP_SUCCESS = 0
 HIP_ERROR_INVALID_VALUE = 1
 
-EXPORTED = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name")
+EXPORTED = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name",
+            "sgemm_f32_mfma_tiles", "sgemm_f32_mfma_tile_name", "sgemm_f32_mfma_select",
+            "sgemm_f32_mfma_tile")
 
 _lib = None
 
@@ -64,6 +66,14 @@ def lib() -> ctypes.CDLL:
         l.sgemm_f32_select.restype = i
         l.sgemm_f32_algo_name.argtypes = [i]
         l.sgemm_f32_algo_name.restype = ctypes.c_char_p
+        l.sgemm_f32_mfma_tiles.argtypes = []
+        l.sgemm_f32_mfma_tiles.restype = i
+        l.sgemm_f32_mfma_tile_name.argtypes = [i]
+        l.sgemm_f32_mfma_tile_name.restype = ctypes.c_char_p
+        l.sgemm_f32_mfma_select.argtypes = [i, i, i, i]
+        l.sgemm_f32_mfma_select.restype = i
+        l.sgemm_f32_mfma_tile.argtypes = args + [i]
+        l.sgemm_f32_mfma_tile.restype = i
         _lib = l
     return _lib
 
@@ -85,3 +95,24 @@ def sgemm_f32_select(M, N, K, A, lda, B, ldb, C, ldc) -> int:
 
 def sgemm_f32_algo_name(algo: int) -> str:
     return lib().sgemm_f32_algo_name(algo).decode()
+
+
+def sgemm_f32_mfma_tiles() -> int:
+    """Number of tile configurations of the matrix-core rung."""
+    return lib().sgemm_f32_mfma_tiles()
+
+
+def sgemm_f32_mfma_tile_name(tile: int):
+    """Description of configuration `tile`, or None for an unknown id."""
+    r = lib().sgemm_f32_mfma_tile_name(tile)
+    return None if r is None else r.decode()
+
+
+def sgemm_f32_mfma_select(M, N, K, compute_units=256) -> int:
+    """Configuration id the matrix-core rung uses for this shape (host-only)."""
+    return lib().sgemm_f32_mfma_select(M, N, K, compute_units)
+
+
+def sgemm_f32_mfma_tile(M, N, K, A, lda, B, ldb, C, ldc, stream=0, tile=0) -> int:
+    """C = A·B on the matrix-core rung with configuration `tile`; returns the hipError_t."""
+    return lib().sgemm_f32_mfma_tile(M, N, K, A, lda, B, ldb, C, ldc, stream, tile)

@@ -38,6 +38,12 @@ hipError_t launch_naive(const Problem &p, hipStream_t s);
 hipError_t launch_lds_tiled(const Problem &p, hipStream_t s);
 hipError_t launch_valu_regblock(const Problem &p, hipStream_t s);
 hipError_t launch_mfma(const Problem &p, hipStream_t s);
+// The MFMA rung with one tile configuration forced (0 <= tile < mfma_tile_count()).
+hipError_t launch_mfma_tile(const Problem &p, hipStream_t s, int tile);
+int mfma_tile_count();
+const char *mfma_tile_name(int tile);
+// The configuration launch_mfma() uses for this shape on `cus` compute units.
+int mfma_select(int M, int N, int K, int cus);
 hipError_t launch_skinny(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_n(const Problem &p, hipStream_t s);
 

@@ -37,6 +37,7 @@
 // partial tiles), so no value outside the logical matrices enters a stored
 // result and no load leaves the matrices' extents.
 #include <cmath>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -50,11 +51,19 @@ template <int N> struct VecOf;
 template <> struct VecOf<1> { typedef float type; };
 template <> struct VecOf<2> { typedef f32x2 type; };
 template <> struct VecOf<4> { typedef f32x4 type; };
+// Three adjacent floats, 4-byte aligned: read from LDS as a two-dword and a
+// one-dword access.
+struct F3 {
+    float e[3];
+};
+template <> struct VecOf<3> { typedef F3 type; };
 
 template <int N>
 __device__ __forceinline__ float lane_of(const typename VecOf<N>::type &v, int j) {
     if constexpr (N == 1) {
         return v;
+    } else if constexpr (N == 3) {
+        return v.e[j];
     } else {
         return v[j];
     }
@@ -121,11 +130,18 @@ struct MfmaTile {
     static constexpr int B_VECS = (B_TOTAL + THREADS - 1) / THREADS;
     static constexpr int STEPS = BK / (8 * KW);          // 8-wide k steps per group per window
     static constexpr int MF = 4 * TM * TN;               // MFMAs per step
-    static constexpr int DSR = TM + 4;                   // LDS reads per step
+    static constexpr int DSR = TM + 4 * (TN == 3 ? 2 : 1);  // LDS reads per step
     static constexpr int DSW = A_VECS + B_VECS;          // LDS writes per window
     static constexpr int VMR = A_VECS + B_VECS;          // global loads per window
+    // The steady-state loop writes LDS in the first step of a window and issues
+    // the `vmr` global loads of a later window in the same step, or in the second
+    // step when one step has too few MFMAs to cover all of those memory
+    // instructions.
+    static constexpr int load_step(int vmr) {
+        return (STEPS > 1 && MF < DSR + DSW + vmr) ? 1 : 0;
+    }
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0, "wave tiling");
-    static_assert(TN == 1 || TN == 2 || TN == 4, "a lane holds 1, 2 or 4 adjacent columns");
+    static_assert(TN >= 1 && TN <= 4, "a lane holds 1 to 4 adjacent columns");
     static_assert(BK % (8 * KW) == 0 && BK % 4 == 0, "k window splits into 8-wide steps");
     static_assert(THREADS <= 1024, "work-group size");
     static_assert(PAD_A_ % 4 == 0 && PAD_B_ % 4 == 0, "16-byte aligned LDS rows");
@@ -310,13 +326,24 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
     int w = w_begin;
     if constexpr (T::STAGES == 3) read_frag(frag[0], lds, 0);
 
-    // Steady state: a work-group whose columns lie inside B, on a window whose
-    // successors up to w + STAGES are all full.  The body has no branches, so
-    // the copies of later windows (LDS stores of window w + STAGES - 1, global
-    // loads of window w + STAGES) and the fragment reads of the next step are
-    // spread one by one between the MFMAs of the first step instead of
-    // stalling the matrix cores in a block of their own.
-    if (cols_inside) {
+    // Steady state: a window whose successors up to w + STAGES are all full.
+    // The body has no branches, so the copies of later windows (LDS stores of
+    // window w + STAGES - 1, global loads of window w + STAGES) and the fragment
+    // reads of the next step are spread one by one between the MFMAs instead of
+    // stalling the matrix cores in a block of their own.  Work-groups on the
+    // right edge of C (EDGE) load B one element at a time with the column index
+    // clamped to N - 1, which keeps the body free of branches there too.
+    auto steady = [&](auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        constexpr int VMR = EDGE ? T::A_VECS + 4 * T::B_VECS : T::VMR;
+        constexpr int LOAD_STEP = T::load_step(VMR);
+        int b_off[T::B_VECS][4];
+        if constexpr (EDGE) {
+#pragma unroll
+            for (int v = 0; v < T::B_VECS; ++v)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) b_off[v][e] = min(b_n[v] + e, N - 1) - b_n[v];
+        }
         const int steady_end = min(w_end, K / T::BK) - T::STAGES;
         for (; w < steady_end; ++w) {
             const float *s = lds + cur * T::STAGE;
@@ -330,20 +357,34 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
                 } else if constexpr (T::STAGES == 3) {
                     read_frag(frag[(t + 1) & 1], lds + next * T::STAGE, 0);
                 }
-                if (t == 0) {
-                    stash(fill);
+                if (t == 0) stash(fill);
+                if (t == LOAD_STEP) {
                     const int64_t k0 = (int64_t)(w + T::STAGES) * T::BK;
 #pragma unroll
                     for (int v = 0; v < T::A_VECS; ++v) ra[v] = load16(a_src[v] + k0);
 #pragma unroll
-                    for (int v = 0; v < T::B_VECS; ++v) rb[v] = load16(b_src[v] + k0 * ldb);
+                    for (int v = 0; v < T::B_VECS; ++v) {
+                        const float *p = b_src[v] + k0 * ldb;
+                        if constexpr (EDGE) {
+                            rb[v].x = p[b_off[v][0]];
+                            rb[v].y = p[b_off[v][1]];
+                            rb[v].z = p[b_off[v][2]];
+                            rb[v].w = p[b_off[v][3]];
+                        } else {
+                            rb[v] = load16(p);
+                        }
+                    }
                 }
                 multiply(frag[t & 1]);
                 // LDS reads issued in step 0, in a middle step and in the last step.
                 constexpr int R0 = (1 < T::STEPS || T::STAGES == 3) ? T::DSR : 0;
                 constexpr int RL = T::STAGES == 3 ? T::DSR : 0;
+                constexpr int R1 = 2 < T::STEPS ? T::DSR : RL;
+                constexpr int VM0 = LOAD_STEP == 0 ? VMR : 0;
                 if (t == 0) {
-                    interleave<T::MF, R0, T::DSW, T::VMR>();
+                    interleave<T::MF, R0, T::DSW, VM0>();
+                } else if (t == LOAD_STEP) {
+                    interleave<T::MF, R1, 0, VMR>();
                 } else if (t + 1 < T::STEPS) {
                     interleave<T::MF, T::DSR, 0, 0>();
                 } else {
@@ -354,10 +395,15 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
             __syncthreads();
             cur = next;
         }
+    };
+    if (cols_inside) {
+        steady(std::false_type{});
+    } else {
+        steady(std::true_type{});
     }
 
-    // Remaining windows (the last STAGES ones, a partial last window, work-groups
-    // on the right edge of C): the same schedule with the copies guarded.
+    // Remaining windows (the last STAGES ones and a partial last window): the
+    // same schedule with the copies guarded.
     for (; w < w_end; ++w) {
         const float *s = lds + cur * T::STAGE;
         const int next = cur + 1 == T::STAGES ? 0 : cur + 1;
@@ -509,49 +555,50 @@ static hipError_t launch_tile(const Problem &p, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Tile choice.  A launch of T tiles on U compute units finishes when the busiest
-// CU has worked through ceil(T / U) tiles, so a configuration's time is modelled
-// as ceil(T / U) * 2*BM*BN*K / (e / 256) + t0, where e is a whole-chip throughput
-// in TFLOP/s and t0 a fixed cost per launch (ramp-up, prologue, epilogue).  Each
-// configuration has two throughputs: one for products whose A and B together
-// fit in 200 MB (inside the 256 MB Infinity Cache), one for larger products.
-// All three numbers per configuration were fitted to timings of every
-// configuration on 15 shapes on MI355X (the 512^3, 1024^3, 2048 x 3072 x 4096,
-// 4095 x 4097 x 1023 and 8192^3 products among them); on each of those shapes
-// the model picks the fastest measured configuration.  The smallest estimate
-// wins.
+// CU has worked through R = ceil(T / U) tiles, so a configuration's time is
+// modelled as R * (2*BM*BN*K / (e / 256) + t1) + t0, where e is a whole-chip
+// throughput in TFLOP/s, t1 a fixed cost per tile (prologue, epilogue) and t0 a
+// fixed cost per launch.  Each configuration has two throughputs: one for
+// products whose A and B together fit in 200 MB (inside the 256 MB Infinity
+// Cache), one for larger products.  The four numbers per configuration were
+// fitted (least squares on log time) to timings of every configuration on 14
+// shapes on MI355X, among them the 512^3, 1024^3, 2048 x 3072 x 4096,
+// 4095 x 4097 x 1023 and 8192^3 products; on 12 of them the model picks the
+// fastest configuration and on the other two one within 3% of it.  The smallest
+// estimate wins.
 struct TileChoice {
     hipError_t (*launch)(const Problem &, hipStream_t);
+    const char *name;  // block, k window, wave block, wave groups, LDS stages
     int bm, bn;
     double tflops_cached;  // e, A and B within 200 MB
     double tflops_large;   // e, larger A and B
     double t0_us;          // t0
+    double t1_us;          // t1
 };
 
 // 256 x 256 blocks, one wave per SIMD with 128 x 128 of C each: large products.
 using TileHuge = MfmaTile<256, 256, 16, 128, 128, 1, 8, 3>;
-using TileLarge = MfmaTile<256, 128, 16, 128, 64, 1, 8, 3>;
 using TileWide = MfmaTile<128, 128, 16, 32, 128, 1, 8, 3>;
-// 128 x 192 blocks, k split over two wave groups: one block per CU on grids of
-// about 256 blocks, such as 2048 x 3072.
-using TileSplit192 = MfmaTile<128, 192, 32, 64, 64, 2, 8, 3>;
-using TileMid = MfmaTile<64, 128, 16, 32, 64, 1, 8, 3>;
+// 128 x 192 blocks of 64 x 96 per wave, k split over two wave groups (two waves
+// per SIMD): one block per CU on grids of about 256 blocks, such as 2048 x 3072.
+using TileSplit192 = MfmaTile<128, 192, 32, 64, 96, 2, 8, 3>;
+// 192 x 128 blocks of 96 x 64 per wave.
+using TileTall = MfmaTile<192, 128, 16, 96, 64, 1, 8, 3>;
 using TileSmall = MfmaTile<64, 64, 16, 32, 32, 1, 4, 3>;
 using TileSplit64 = MfmaTile<64, 64, 32, 32, 32, 2, 4, 3>;
 // k split four ways: one 8-wide step per group and window, so two stages.
-using TileSplit64x4 = MfmaTile<64, 64, 32, 32, 64, 4, 4, 2>;
 using TileTiny = MfmaTile<32, 32, 32, 32, 32, 4, 4, 2>;
 
 static const TileChoice kTiles[] = {
-    {launch_tile<TileHuge>, 256, 256, 132.0, 150.0, 11.0},
-    {launch_tile<TileLarge>, 256, 128, 123.0, 145.0, 7.0},
-    {launch_tile<TileWide>, 128, 128, 123.0, 139.0, 4.0},
-    {launch_tile<TileSplit192>, 128, 192, 119.0, 104.0, 18.0},
-    {launch_tile<TileMid>, 64, 128, 112.0, 109.0, 8.0},
-    {launch_tile<TileSmall>, 64, 64, 115.0, 120.0, 9.0},
-    {launch_tile<TileSplit64>, 64, 64, 115.0, 127.0, 6.0},
-    {launch_tile<TileSplit64x4>, 64, 64, 110.0, 123.0, 7.0},
-    {launch_tile<TileTiny>, 32, 32, 99.0, 105.0, 7.0},
+    {launch_tile<TileHuge>, "256x256x16 w128x128 k1 s3", 256, 256, 148.5, 150.0, 4.0, 15.0},
+    {launch_tile<TileWide>, "128x128x16 w32x128 k1 s3", 128, 128, 136.5, 137.5, 6.0, 2.0},
+    {launch_tile<TileSplit192>, "128x192x32 w64x96 k2 s3", 128, 192, 138.5, 138.5, 5.0, 9.0},
+    {launch_tile<TileTall>, "192x128x16 w96x64 k1 s3", 192, 128, 138.5, 143.0, 7.0, 3.0},
+    {launch_tile<TileSmall>, "64x64x16 w32x32 k1 s3", 64, 64, 128.0, 122.5, 8.0, 1.0},
+    {launch_tile<TileSplit64>, "64x64x32 w32x32 k2 s3", 64, 64, 125.0, 129.5, 6.0, 1.0},
+    {launch_tile<TileTiny>, "32x32x32 w32x32 k4 s2", 32, 32, 101.0, 106.0, 7.0, 0.0},
 };
+constexpr int kTileCount = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
 
 static int compute_units() {
     int dev = 0, cus = 0;
@@ -566,14 +613,15 @@ static int compute_units() {
 static int choose_tile(int M, int N, int K, int cus) {
     int best = 0;
     double best_us = 0;
-    for (int i = 0; i < (int)(sizeof(kTiles) / sizeof(kTiles[0])); ++i) {
+    for (int i = 0; i < kTileCount; ++i) {
         const TileChoice &c = kTiles[i];
         const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         const double per_cu = std::ceil(tiles / cus);
         const double operands = 4.0 * ((double)M * K + (double)K * N);
         const double per_cu_tflops =
             (operands <= 200e6 ? c.tflops_cached : c.tflops_large) / 256.0;  // fitted on 256 CUs
-        const double us = per_cu * 2.0 * c.bm * c.bn * (double)K / (per_cu_tflops * 1e6) + c.t0_us;
+        const double us =
+            per_cu * (2.0 * c.bm * c.bn * (double)K / (per_cu_tflops * 1e6) + c.t1_us) + c.t0_us;
         if (i == 0 || us < best_us) {
             best = i;
             best_us = us;
@@ -584,6 +632,19 @@ static int choose_tile(int M, int N, int K, int cus) {
 
 hipError_t launch_mfma(const Problem &p, hipStream_t s) {
     return kTiles[choose_tile(p.M, p.N, p.K, compute_units())].launch(p, s);
+}
+
+int mfma_tile_count() { return kTileCount; }
+
+const char *mfma_tile_name(int tile) {
+    return tile >= 0 && tile < kTileCount ? kTiles[tile].name : nullptr;
+}
+
+int mfma_select(int M, int N, int K, int cus) { return choose_tile(M, N, K, cus > 0 ? cus : 256); }
+
+hipError_t launch_mfma_tile(const Problem &p, hipStream_t s, int tile) {
+    if (tile < 0 || tile >= kTileCount) return hipErrorInvalidValue;
+    return kTiles[tile].launch(p, s);
 }
 
 }  // namespace sgemm

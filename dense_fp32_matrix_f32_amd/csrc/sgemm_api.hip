@@ -91,3 +91,24 @@ extern "C" hipError_t sgemm_f32(int M, int N, int K, const float *A, int lda, co
                                 int ldb, float *C, int ldc, hipStream_t stream) {
     return sgemm_f32_algo(M, N, K, A, lda, B, ldb, C, ldc, stream, SGEMM_F32_ALGO_AUTO);
 }
+
+extern "C" int sgemm_f32_mfma_tiles(void) { return sgemm::mfma_tile_count(); }
+
+extern "C" const char *sgemm_f32_mfma_tile_name(int tile) { return sgemm::mfma_tile_name(tile); }
+
+extern "C" int sgemm_f32_mfma_select(int M, int N, int K, int compute_units) {
+    if (M < 0 || N < 0 || K < 0) return -1;
+    return sgemm::mfma_select(M, N, K, compute_units);
+}
+
+extern "C" hipError_t sgemm_f32_mfma_tile(int M, int N, int K, const float *A, int lda,
+                                          const float *B, int ldb, float *C, int ldc,
+                                          hipStream_t stream, int tile) {
+    if (tile < 0 || tile >= sgemm::mfma_tile_count()) return hipErrorInvalidValue;
+    const hipError_t v = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (v != hipSuccess) return v;
+    if (M == 0 || N == 0) return hipSuccess;
+    const Problem p{M, N, K, A, lda, B, ldb, C, ldc};
+    if (K == 0) return sgemm::launch_zero_fill(p, stream);
+    return sgemm::launch_mfma_tile(p, stream, tile);
+}

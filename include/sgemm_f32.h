@@ -100,6 +100,36 @@ int sgemm_f32_select(int M, int N, int K,
 /* Static, NUL-terminated name of an algorithm id ("invalid" if unknown). */
 const char *sgemm_f32_algo_name(int algo);
 
+/*
+ * Tile configurations of the matrix-core rung (SGEMM_F32_ALGO_MFMA), for
+ * tuning and tests.  The rung tiles C into BM x BN blocks, one work-group per
+ * block, as in the shared-memory tiling of the page "CUDA算子优化(4)：矩阵乘法"
+ * (section "版本V1共享内存分块"); a configuration fixes the block and k-window
+ * sizes, the block of C held by each wave, the number of wave groups that split
+ * each k window, and the number of LDS stages.  SGEMM_F32_ALGO_MFMA picks one
+ * from a cost model of the shape.
+ *
+ * sgemm_f32_mfma_tiles()      number of configurations (ids 0 .. count-1).
+ * sgemm_f32_mfma_tile_name()  static description such as
+ *                             "256x256x16 w128x128 k1 s3" (BM x BN x BK, wave
+ *                             block, wave groups, stages); NULL for an unknown id.
+ * sgemm_f32_mfma_select()     the id SGEMM_F32_ALGO_MFMA uses for an M x N x K
+ *                             product on a device with `compute_units` CUs
+ *                             (<= 0 means 256); host-only, no HIP call; -1 if
+ *                             M, N or K is negative.
+ * sgemm_f32_mfma_tile()       same operation and contract as sgemm_f32(), on the
+ *                             matrix-core rung with configuration `tile`; an
+ *                             unknown id is hipErrorInvalidValue.
+ */
+int sgemm_f32_mfma_tiles(void);
+const char *sgemm_f32_mfma_tile_name(int tile);
+int sgemm_f32_mfma_select(int M, int N, int K, int compute_units);
+hipError_t sgemm_f32_mfma_tile(int M, int N, int K,
+                               const float *A, int lda,
+                               const float *B, int ldb,
+                               float *C, int ldc,
+                               hipStream_t stream, int tile);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,16 @@ class Device:
             raise sg.SgemmError(st)
         s.synchronize()
 
+    def run_tile(self, tile, stream=None):
+        """The matrix-core rung with tile configuration `tile` forced."""
+        torch = self.torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        st = sg.sgemm_f32_mfma_tile(self.M, self.N, self.K, self.a_ptr, self.lda, self.b_ptr,
+                                    self.ldb, self.c_ptr, self.ldc, s.cuda_stream, tile)
+        if st != 0:
+            raise sg.SgemmError(st, "sgemm_f32_mfma_tile")
+        s.synchronize()
+
     def result(self):
         """(C as M x N float32, guard-band contents) on the host."""
         full = self.c_buf.cpu().numpy()[self.offset:].reshape(self.M + 2, self.ldc)

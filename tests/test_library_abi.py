@@ -2,6 +2,7 @@
 choice and the work-group -> tile mapping.  No kernel is launched."""
 import ctypes
 import glob
+import json
 import os
 import re
 import subprocess
@@ -120,3 +121,68 @@ def test_tile_order_is_a_bijection(tmp_path):
     shapes += [32, 33, 8, 64, 32, 8, 16, 16, 8]   # the ragged and 8192^3 grids
     out = subprocess.run([str(exe), *map(str, shapes)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout[-2000:]
+
+
+def test_mfma_tile_table():
+    n = sg.sgemm_f32_mfma_tiles()
+    assert n >= 1
+    names = [sg.sgemm_f32_mfma_tile_name(t) for t in range(n)]
+    assert len(set(names)) == n
+    for name in names:
+        assert re.fullmatch(r"\d+x\d+x\d+ w\d+x\d+ k\d s[23]", name), name
+    assert sg.sgemm_f32_mfma_tile_name(n) is None
+    assert sg.sgemm_f32_mfma_tile_name(-1) is None
+
+
+def _tile_of(M, N, K, cus=256):
+    return sg.sgemm_f32_mfma_tile_name(sg.sgemm_f32_mfma_select(M, N, K, cus))
+
+
+def test_mfma_tile_selection():
+    # 8192^3: 1024 blocks of 256 x 256, four per CU.
+    assert _tile_of(8192, 8192, 8192).startswith("256x256x")
+    # 2048 x 3072: 256 blocks of 128 x 192, one per CU.
+    assert _tile_of(2048, 3072, 4096).startswith("128x192x")
+    # 512^3: too few blocks for large tiles; the smallest blocks fill the chip.
+    assert _tile_of(512, 512, 512).startswith("32x32x")
+    assert sg.sgemm_f32_mfma_select(-1, 8, 8, 256) == -1
+    for shape in [(1, 1, 1), (9, 9, 1), (4095, 4097, 1023), (100000, 9, 3), (9, 100000, 3)]:
+        assert 0 <= sg.sgemm_f32_mfma_select(*shape, 256) < sg.sgemm_f32_mfma_tiles()
+    # a device with fewer CUs still gets a valid choice
+    assert 0 <= sg.sgemm_f32_mfma_select(8192, 8192, 8192, 0) < sg.sgemm_f32_mfma_tiles()
+    assert 0 <= sg.sgemm_f32_mfma_select(8192, 8192, 8192, 80) < sg.sgemm_f32_mfma_tiles()
+
+
+def test_mfma_tile_entry_validates():
+    n = sg.sgemm_f32_mfma_tiles()
+    for tile in (-1, n):
+        assert sg.sgemm_f32_mfma_tile(8, 8, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR, 8, 0, tile) == INVALID
+    assert sg.sgemm_f32_mfma_tile(8, 8, 8, A_ADDR, 7, B_ADDR, 8, C_ADDR, 8, 0, 0) == INVALID
+    assert sg.sgemm_f32_mfma_tile(8, 8, 8, A_ADDR, 8, B_ADDR, 8, A_ADDR + 4, 8, 0, 0) == INVALID
+    assert sg.sgemm_f32_mfma_tile(0, 8, 8, 0, 8, 0, 8, 0, 8, 0, 0) == 0
+
+
+def _tile_timings():
+    rows = {}
+    path = os.path.join(ROOT, "tests", "data", "mfma_tile_timings.txt")
+    for line in open(path, encoding="utf-8"):
+        if line.startswith("{"):
+            r = json.loads(line)
+            rows.setdefault(tuple(r["shape"]), {})[r["name"]] = r["kernel_ms_avg"]
+    return rows
+
+
+def test_mfma_tile_choice_against_measured_timings():
+    """On each measured shape the model's configuration is within 5% of the fastest
+    one, and at least 12 of the 15 choices are the fastest outright."""
+    timings = _tile_timings()
+    assert len(timings) == 15
+    exact = 0
+    for shape, by_name in timings.items():
+        assert set(by_name) == {sg.sgemm_f32_mfma_tile_name(t)
+                                for t in range(sg.sgemm_f32_mfma_tiles())}
+        chosen = sg.sgemm_f32_mfma_tile_name(sg.sgemm_f32_mfma_select(*shape, 256))
+        best = min(by_name.values())
+        assert by_name[chosen] <= 1.05 * best, (shape, chosen, by_name)
+        exact += by_name[chosen] == best
+    assert exact >= 12
