@@ -98,10 +98,10 @@ def host_threads() -> int:
         return max(1, os.cpu_count() or 1)
 
 
-def make_inputs(torch, M, N, K, seed):
+def make_inputs(torch, M, N, K, seed, dist="normal"):
     import synthgen
-    A = synthgen.matrix(M, K, seed=seed, stream=0, dist="normal")
-    B = synthgen.matrix(K, N, seed=seed, stream=1, dist="normal")
+    A = synthgen.matrix(M, K, seed=seed, stream=0, dist=dist)
+    B = synthgen.matrix(K, N, seed=seed, stream=1, dist=dist)
     dA = torch.from_numpy(A).cuda()
     dB = torch.from_numpy(B).cuda()
     dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
@@ -193,6 +193,111 @@ def ladder(torch, sg, M, N, K, args):
                           "steps": steps, "warmup": warm}), flush=True)
 
 
+# The five workloads: name, M, N, K, input distribution, seed (A is stream 0 and
+# B stream 1 of the seeded generator).
+CONFIGS = [("c1", 512, 512, 512, "normal", 1), ("c2", 1024, 1024, 1024, "normal", 2),
+           ("c3", 2048, 3072, 4096, "normal", 3), ("c4a", 4095, 4097, 1023, "uniform_pm1", 4),
+           ("c4b", 1, 4096, 4096, "uniform_pm1", 5), ("c5", 8192, 8192, 8192, "normal", 6)]
+
+
+def gpu_sclk(torch):
+    """Current shader clock level of device 0 as the driver reports it, or None."""
+    try:
+        p = torch.cuda.get_device_properties(0)
+        path = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
+                f"{p.pci_device_id:02x}.0/pp_dpm_sclk")
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return line.split(":", 1)[1].strip(" *\n")
+    except Exception:  # noqa: BLE001 -- informational only
+        return None
+    return None
+
+
+def timed_launches(torch, stream, launch, warm_ms=300.0, timed_ms=200.0, min_steps=20):
+    """Per-launch HIP-event times (ms) after a time-based warm-up."""
+    def run(n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            launch()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+    est = max(min(run(3)), 1e-3)
+    run(max(1, min(20000, int(warm_ms / est))))
+    return run(max(min_steps, min(20000, int(timed_ms / est))))
+
+
+def config_report(torch, sg, args):
+    """One JSON line per workload: kernel time (median, mean, min of per-launch
+    events), TFLOP/s and GB/s against the peaks, the algorithm and tile used; for
+    the 1 x 4096 x 4096 product also with B rotated over five buffers (320 MB, more
+    than the 256 MB Infinity Cache), and for 512^3 and 1024^3 the oracle on one
+    host thread and on all of them."""
+    import statistics
+
+    stream = torch.cuda.current_stream()
+    print(json.dumps({"sclk_before": gpu_sclk(torch)}), flush=True)
+    for name, M, N, K, dist, seed in CONFIGS:
+        A, B, dA, dB, dC = make_inputs(torch, M, N, K, seed, dist)
+        algo = sg.sgemm_f32_select(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N)
+
+        def launch(b_ptr=None):
+            st = sg.sgemm_f32(M, N, K, dA.data_ptr(), K, b_ptr or dB.data_ptr(), N,
+                              dC.data_ptr(), N, stream.cuda_stream)
+            if st != 0:
+                raise sg.SgemmError(st)
+
+        kms = timed_launches(torch, stream, launch)
+        med = statistics.median(kms)
+        flops, nbytes = algorithmic_flops(M, N, K), algorithmic_bytes(M, N, K)
+        rec = {"config": name, "shape": [M, N, K], "dist": dist, "seed": seed,
+               "algo": sg.sgemm_f32_algo_name(algo),
+               "tile": sg.sgemm_f32_mfma_tile_name(sg.sgemm_f32_mfma_select(
+                   M, N, K, torch.cuda.get_device_properties(0).multi_processor_count))
+               if algo == sg.ALGO_MFMA else None,
+               "kernel_ms_median": round(med, 5), "kernel_ms_mean": round(sum(kms) / len(kms), 5),
+               "kernel_ms_min": round(min(kms), 5), "launches": len(kms),
+               "tflops": round(flops / (med * 1e-3) / 1e12, 3),
+               "pct_fp32_peak": round(100 * flops / (med * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 2),
+               "gbs": round(nbytes / (med * 1e-3) / 1e9, 1),
+               "pct_hbm_peak": round(100 * nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+               "intensity_flop_per_byte": round(intensity(M, N, K), 2)}
+        if name == "c4b":
+            import synthgen
+            bufs = [dB] + [torch.from_numpy(synthgen.matrix(K, N, seed=seed + 100 + i, stream=1,
+                                                            dist=dist)).cuda() for i in range(4)]
+            turn = [0]
+
+            def rotated():
+                launch(bufs[turn[0] % len(bufs)].data_ptr())
+                turn[0] += 1
+            rms = timed_launches(torch, stream, rotated)
+            rmed = statistics.median(rms)
+            rec["rotated"] = {"b_buffers": len(bufs), "bytes": 4 * K * N * len(bufs),
+                              "kernel_ms_median": round(rmed, 5),
+                              "kernel_ms_min": round(min(rms), 5),
+                              "gbs": round(nbytes / (rmed * 1e-3) / 1e9, 1),
+                              "pct_hbm_peak": round(100 * nbytes / (rmed * 1e-3) / 1e9 /
+                                                    PEAK_HBM_GBS, 2)}
+            del bufs
+        if name in ("c1", "c2") and args.cpu_seconds > 0:
+            import oracle
+            for threads in (1, host_threads()):
+                t0 = time.perf_counter()
+                oracle.sgemm(A[:, :K], B[:, :N], threads=threads)
+                t = time.perf_counter() - t0
+                rec[f"oracle_{'1' if threads == 1 else 'all'}_thread"] = {
+                    "threads": threads, "ms": round(t * 1e3, 1),
+                    "gflops": round(flops / t / 1e9, 3)}
+        del dA, dB, dC
+        print(json.dumps(rec), flush=True)
+    print(json.dumps({"sclk_after": gpu_sclk(torch)}), flush=True)
+
+
 # Shapes of the tile-choice model: the five workloads and nine others that mix
 # wave quantisation, ragged edges, short and long k, and cached and uncached sizes.
 TILE_SHAPES = [(8192, 8192, 8192), (2048, 3072, 4096), (4095, 4097, 1023), (1024, 1024, 1024),
@@ -259,6 +364,9 @@ def main(argv=None):
     p.add_argument("--ladder", action="store_true",
                    help="time every algorithm of the ladder on --shape instead (one JSON line "
                         "per algorithm)")
+    p.add_argument("--configs", action="store_true",
+                   help="report every workload (512^3, 1024^3, 2048x3072x4096, 4095x4097x1023, "
+                        "1x4096x4096, 8192^3) instead, one JSON line each")
     p.add_argument("--tiles", action="store_true",
                    help="time every tile configuration of the matrix-core rung on --shape, or on "
                         "the tile-model shapes with --shape all (one JSON line per configuration)")
@@ -287,6 +395,9 @@ def main(argv=None):
         print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 3}), flush=True)
         return
 
+    if args.configs:
+        config_report(torch, sg, args)
+        return
     if args.tiles:
         shapes = TILE_SHAPES if args.shape == "all" else \
             [tuple(int(x) for x in args.shape.split(","))]
