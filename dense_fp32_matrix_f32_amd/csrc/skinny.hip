@@ -9,6 +9,8 @@
 // pairwise reduction in LDS, so results are reproducible and no atomics are
 // needed.  Up to 1024 work-items per group keep enough 16-byte loads in flight
 // per CU to cover HBM latency.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace sgemm {
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
     constexpr int CW = 4 * LPR;        // columns per work-group
     constexpr int S = THREADS / LPR;   // k slots (a power of two)
     constexpr int OUT = MR * CW;       // outputs per work-group
-    constexpr int U = 8;               // independent loads in flight per work-item
+    constexpr int U = MR <= 2 ? 16 : 8;  // k values per batch (loads in flight) per work-item
     static_assert((S & (S - 1)) == 0, "slot count is a power of two");
     __shared__ float red[S][OUT + 1];
 
@@ -50,36 +52,64 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[m][0] = acc[m][1] = acc[m][2] = acc[m][3] = 0.0f;
 
-    auto load_b = [&](int k) -> f32x4 {
-        const float *row = B + (int64_t)k * ldb;
-        if (vec) return load16_skinny(row + n);
-        f32x4 v;
-        v.x = row[min(n + 0, N - 1)];
-        v.y = row[min(n + 1, N - 1)];
-        v.z = row[min(n + 2, N - 1)];
-        v.w = row[min(n + 3, N - 1)];
-        return v;
-    };
-    auto fma4 = [&](int k, const f32x4 &b) {
+    // One pass over this work-item's k values.  VEC: its four columns lie inside
+    // B (every work-item but those at the right edge), read as one 16-byte load;
+    // otherwise column indices are clamped to N - 1 (those outputs are not stored).
+    // All loads of a batch of U k values are issued before any of them is used,
+    // so U loads of B and U*MR values of A are in flight together.
+    auto pass = [&](auto vec_tag) {
+        constexpr bool VEC = decltype(vec_tag)::value;
+        int cn[4];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            const float a = arow[m][k];
-            acc[m][0] = fmaf(a, b.x, acc[m][0]);
-            acc[m][1] = fmaf(a, b.y, acc[m][1]);
-            acc[m][2] = fmaf(a, b.z, acc[m][2]);
-            acc[m][3] = fmaf(a, b.w, acc[m][3]);
+        for (int e = 0; e < 4; ++e) cn[e] = min(n + e, N - 1);
+        auto load_b = [&](int k) -> f32x4 {
+            const float *row = B + (int64_t)k * ldb;
+            if constexpr (VEC) {
+                return load16_skinny(row + n);
+            } else {
+                f32x4 v;
+                v.x = row[cn[0]];
+                v.y = row[cn[1]];
+                v.z = row[cn[2]];
+                v.w = row[cn[3]];
+                return v;
+            }
+        };
+        auto fma4 = [&](const float (&a)[MR], const f32x4 &b) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                acc[m][0] = fmaf(a[m], b.x, acc[m][0]);
+                acc[m][1] = fmaf(a[m], b.y, acc[m][1]);
+                acc[m][2] = fmaf(a[m], b.z, acc[m][2]);
+                acc[m][3] = fmaf(a[m], b.w, acc[m][3]);
+            }
+        };
+        int k = slot;
+        for (; k + (U - 1) * S < K; k += U * S) {
+            f32x4 b[U];
+            float a[U][MR];
+#pragma unroll
+            for (int u = 0; u < U; ++u) b[u] = load_b(k + u * S);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int m = 0; m < MR; ++m) a[u][m] = arow[m][k + u * S];
+#pragma unroll
+            for (int u = 0; u < U; ++u) fma4(a[u], b[u]);
+        }
+        for (; k < K; k += S) {
+            const f32x4 b = load_b(k);
+            float a[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) a[m] = arow[m][k];
+            fma4(a, b);
         }
     };
-
-    int k = slot;
-    for (; k + (U - 1) * S < K; k += U * S) {
-        f32x4 b[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) b[u] = load_b(k + u * S);
-#pragma unroll
-        for (int u = 0; u < U; ++u) fma4(k + u * S, b[u]);
+    if (vec) {
+        pass(std::true_type{});
+    } else {
+        pass(std::false_type{});
     }
-    for (; k < K; k += S) fma4(k, load_b(k));
 
 #pragma unroll
     for (int m = 0; m < MR; ++m)
