@@ -447,6 +447,11 @@ def main(argv=None):
                      "algorithmic_flops": flops, "algorithmic_bytes": algorithmic_bytes(M, N, K),
                      "intensity_flop_per_byte": round(intensity(M, N, K), 2)},
     }
+    if used in (sg.ALGO_SKINNY, sg.ALGO_SKINNY_N):
+        # few rows or columns: the product streams one operand, so HBM bounds it
+        gbs = algorithmic_bytes(M, N, K) / (kavg * 1e-3) / 1e9
+        rec["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
     del dA, dB, dC
     if not args.no_also:
         m2, n2, k2 = 2048, 3072, 4096
