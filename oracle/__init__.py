@@ -1,4 +1,5 @@
-"""CPU oracle for C = A·B in fp32 (row-major, alpha = 1, beta = 0).
+"""CPU oracle for C = A·B in fp32 (row-major, alpha = 1, beta = 0), and for the
+general form C = alpha·op(A)·op(B) + beta·C.
 
 TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU
@@ -62,6 +63,11 @@ def load(path: str | None = None):
     lib.oracle_sgemm_f64_elems.restype = ctypes.c_int
     lib.oracle_sgemm_f64_elems.argtypes = [i64, i64, i64, vp, i64, vp, i64, i64, vp, vp,
                                            vp, vp, ctypes.c_int]
+    if hasattr(lib, "oracle_sgemm_ex_f64"):
+        d, ci = ctypes.c_double, ctypes.c_int
+        lib.oracle_sgemm_ex_f64.restype = ci
+        lib.oracle_sgemm_ex_f64.argtypes = [ci, ci, i64, i64, i64, d, vp, i64, vp, i64, d, vp,
+                                            i64, i64, vp, vp, vp, i64, vp, i64, ci]
     if path is None:
         _lib = lib
     return lib
@@ -127,6 +133,55 @@ def sgemm_elems(A: np.ndarray, B: np.ndarray, rows, cols, threads: int | None = 
     if rc != 0:
         raise ValueError("oracle_sgemm_f64_elems rejected its arguments")
     return C, S
+
+
+def sgemm_ex(A: np.ndarray, B: np.ndarray, transa: bool = False, transb: bool = False,
+             alpha: float = 1.0, beta: float = 0.0, C: np.ndarray | None = None,
+             rows=None, cols=None, threads: int | None = None, lib=None):
+    """Return (C_out, S) in float64 for C_out = alpha*op(A)*op(B) + beta*C.
+
+    A and B are the stored arrays: op(A) is A (M x K) or, with transa, the
+    transpose of the K x M array A; op(B) is B (K x N) or, with transb, the
+    transpose of the N x K array B.  C (M x N float32) is read only when
+    beta != 0.  alpha and beta are rounded to float32 first, as the GPU
+    boundary takes them.  With rows/cols, only the listed elements are
+    computed and returned as vectors.
+    """
+    pa, ra, ca, lda = _operand(A)
+    pb, rb, cb, ldb = _operand(B)
+    M, K = (ca, ra) if transa else (ra, ca)
+    K2, N = (cb, rb) if transb else (rb, cb)
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    alpha = float(np.float32(alpha))
+    beta = float(np.float32(beta))
+    pc, ldcin = 0, max(N, 1)
+    if beta != 0.0 and C is None:
+        raise ValueError("beta != 0 needs C")
+    if C is not None:
+        pc, rc_, cc_, ldcin = _operand(C)
+        if (rc_, cc_) != (M, N):
+            raise ValueError("C has the wrong shape")
+    fn = (lib or load()).oracle_sgemm_ex_f64
+    if rows is None:
+        out = np.empty((M, N), dtype=np.float64)
+        S = np.empty((M, N), dtype=np.float64)
+        rc = fn(int(transa), int(transb), M, N, K, alpha, pa, lda, pb, ldb, beta, pc, ldcin,
+                0, None, None, out.ctypes.data, max(N, 1), S.ctypes.data, max(N, 1),
+                _threads(threads))
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        c = np.ascontiguousarray(cols, dtype=np.int64)
+        if r.shape != c.shape or r.ndim != 1:
+            raise ValueError("rows and cols must be 1-D and of equal length")
+        out = np.empty(r.shape[0], dtype=np.float64)
+        S = np.empty(r.shape[0], dtype=np.float64)
+        rc = fn(int(transa), int(transb), M, N, K, alpha, pa, lda, pb, ldb, beta, pc, ldcin,
+                r.shape[0], r.ctypes.data, c.ctypes.data, out.ctypes.data, 0, S.ctypes.data, 0,
+                _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle_sgemm_ex_f64 rejected its arguments")
+    return out, S
 
 
 def excess(C_gpu: np.ndarray, C: np.ndarray, S: np.ndarray) -> np.ndarray:

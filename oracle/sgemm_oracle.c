@@ -28,6 +28,20 @@
  * The k order of every sum is 0, 1, ..., K-1, so the full-matrix and the
  * per-element entry points return bit-identical values for the same (i, j).
  *
+ * The general form (oracle_sgemm_ex_f64) is the same definition with the
+ * operands of the BLAS-style boundary that the pages compare against (their
+ * cuBLAS baseline, page "CUDA算子优化(4)：矩阵乘法"):
+ *     C_out[i][j] = alpha * sum_k opA[i][k] * opB[k][j] + beta * C_in[i][j]
+ * where opA = A (M x K, A[i*lda + k]) or, transposed, the K x M array A read
+ * as A[k*lda + i]; likewise opB = B (K x N, B[k*ldb + j]) or the N x K array
+ * B read as B[j*ldb + k].  Readings (the pages never scale or accumulate):
+ *   - beta == 0 means C_in is not read at all, so NaN or Inf there does not
+ *     reach the result; alpha == 0 means A and B are not read (the BLAS
+ *     convention).
+ *   - The scale becomes S = |alpha| * sum_k |opA||opB| + |beta| * |C_in|; the
+ *     two extra fp32 roundings of the scaling and the add stay far below
+ *     5e-4 of it.
+ *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared -pthread sgemm_oracle.c -lm
  */
 #include <math.h>
@@ -142,5 +156,112 @@ int oracle_sgemm_f64_elems(int64_t M, int64_t N, int64_t K,
     if (count == 0) return 0;
     oracle_job proto = {M, N, K, A, lda, B, ldb, C, 0, S, 0, rows, cols, 0, 0};
     run_split(proto, count, nthreads, listed_elements);
+    return 0;
+}
+
+/* ---- general form: alpha * op(A) op(B) + beta * C_in ---- */
+
+typedef struct {
+    int transa, transb;
+    int64_t M, N, K;
+    double alpha, beta;
+    const float *A;
+    int64_t lda;
+    const float *B;
+    int64_t ldb;
+    const float *Cin;
+    int64_t ldcin;
+    double *C;
+    int64_t ldc;
+    double *S;
+    int64_t lds;
+    const int64_t *rows; /* NULL: all of row i, else the listed elements */
+    const int64_t *cols;
+    int64_t first, last;
+} oracle_ex_job;
+
+/* Element (i, j) of the general form, the k sum in order 0 .. K-1. */
+static void oracle_element_ex(const oracle_ex_job *p, int64_t i, int64_t j,
+                              double *c_out, double *s_out) {
+    double c = 0.0;
+    double s = 0.0;
+    if (p->alpha != 0.0) {
+        for (int64_t k = 0; k < p->K; ++k) {
+            double a = p->transa ? (double)p->A[k * p->lda + i] : (double)p->A[i * p->lda + k];
+            double b = p->transb ? (double)p->B[j * p->ldb + k] : (double)p->B[k * p->ldb + j];
+            c += a * b;
+            s += fabs(a) * fabs(b);
+        }
+    }
+    double out = p->alpha * c;
+    double scale = fabs(p->alpha) * s;
+    if (p->beta != 0.0) {
+        double cin = (double)p->Cin[i * p->ldcin + j];
+        out += p->beta * cin;
+        scale += fabs(p->beta) * fabs(cin);
+    }
+    *c_out = out;
+    *s_out = scale;
+}
+
+static void *ex_worker(void *arg) {
+    oracle_ex_job *p = (oracle_ex_job *)arg;
+    if (p->rows == 0) {
+        for (int64_t i = p->first; i < p->last; ++i)
+            for (int64_t j = 0; j < p->N; ++j)
+                oracle_element_ex(p, i, j, &p->C[i * p->ldc + j], &p->S[i * p->lds + j]);
+    } else {
+        for (int64_t e = p->first; e < p->last; ++e)
+            oracle_element_ex(p, p->rows[e], p->cols[e], &p->C[e], &p->S[e]);
+    }
+    return 0;
+}
+
+/*
+ * General form.  With rows == NULL, C[i*ldc + j] and S[i*lds + j] for all
+ * i < M, j < N; otherwise C[e] and S[e] for the count listed elements
+ * (rows[e], cols[e]).  Cin may be NULL when beta == 0; A and B may be NULL
+ * when alpha == 0 or K == 0.  Returns 0, or -1 on inconsistent arguments.
+ */
+int oracle_sgemm_ex_f64(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                        double alpha, const float *A, int64_t lda,
+                        const float *B, int64_t ldb, double beta,
+                        const float *Cin, int64_t ldcin,
+                        int64_t count, const int64_t *rows, const int64_t *cols,
+                        double *C, int64_t ldc, double *S, int64_t lds, int nthreads) {
+    if (M < 0 || N < 0 || K < 0 || count < 0) return -1;
+    if (K > 0 && alpha != 0.0) {
+        if (lda < (transa ? M : K) || ldb < (transb ? K : N)) return -1;
+        if (A == 0 || B == 0) return -1;
+    }
+    if (beta != 0.0 && (Cin == 0 || ldcin < N)) return -1;
+    if (rows == 0 && (ldc < N || lds < N)) return -1;
+    if (rows != 0)
+        for (int64_t e = 0; e < count; ++e)
+            if (rows[e] < 0 || rows[e] >= M || cols[e] < 0 || cols[e] >= N) return -1;
+    int64_t units = rows == 0 ? M : count;
+    if (units == 0 || N == 0) return 0;
+    oracle_ex_job proto = {transa != 0, transb != 0, M, N, K, alpha, beta, A, lda, B, ldb,
+                           Cin, ldcin, C, ldc, S, lds, rows, cols, 0, 0};
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > units) nthreads = (int)units;
+    oracle_ex_job jobs[256];
+    pthread_t tid[256];
+    int started[256];
+    int64_t chunk = (units + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = proto;
+        jobs[t].first = t * chunk;
+        jobs[t].last = jobs[t].first + chunk < units ? jobs[t].first + chunk : units;
+        started[t] = 0;
+        if (jobs[t].first >= jobs[t].last) continue;
+        if (t + 1 < nthreads && pthread_create(&tid[t], 0, ex_worker, &jobs[t]) == 0)
+            started[t] = 1;
+        else
+            ex_worker(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (started[t]) pthread_join(tid[t], 0);
     return 0;
 }

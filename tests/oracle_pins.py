@@ -193,6 +193,100 @@ def pin_empty_sum(lib):
     assert C.shape == (4, 6) and np.all(C == 0) and np.all(S == 0)
 
 
+# ---- the general form: alpha * op(A) op(B) + beta * C ----
+
+def _stored(X, trans):
+    """The array that holds X (M x K) when it is passed transposed or not."""
+    return np.ascontiguousarray(X.T) if trans else X
+
+
+def pin_ex_brute_force(lib):
+    """Tiny shapes, all four operand layouts, several alpha/beta, against exact
+    rational arithmetic: alpha*sum + beta*c in Fractions, within the fp64
+    summation bound (K + 2 roundings of the scale)."""
+    cases = [(3, 4, 5, 1.0, 0.0), (2, 5, 3, -0.5, 1.0), (4, 3, 6, 3.0, -2.25), (1, 1, 7, 0.75, 0.5)]
+    for n, (M, N, K, alpha, beta) in enumerate(cases):
+        X = _gen(M, K, 90 + n, 0, "normal")       # op(A)
+        Y = _gen(K, N, 90 + n, 1, "normal")       # op(B)
+        Cin = _gen(M, N, 90 + n, 2, "normal")
+        for ta in (False, True):
+            for tb in (False, True):
+                C, S = oracle.sgemm_ex(_stored(X, ta), _stored(Y, tb), ta, tb, alpha, beta, Cin,
+                                       lib=lib)
+                for i in range(M):
+                    for j in range(N):
+                        prod = _fraction_product(X, Y, i, j)
+                        sabs = sum((abs(Fraction(float(X[i, k]))) * abs(Fraction(float(Y[k, j])))
+                                    for k in range(K)), Fraction(0))
+                        exact = Fraction(alpha) * prod + Fraction(beta) * Fraction(float(Cin[i, j]))
+                        s_exact = (abs(Fraction(alpha)) * sabs +
+                                   abs(Fraction(beta)) * abs(Fraction(float(Cin[i, j]))))
+                        bound = Fraction((K + 2) * 2.0 ** -53 * float(s_exact) * 1.0001)
+                        assert abs(Fraction(C[i, j]) - exact) <= bound, (ta, tb, M, N, K, i, j)
+                        assert abs(Fraction(S[i, j]) - s_exact) <= bound, (ta, tb, i, j)
+
+
+def pin_ex_library_fp64(lib):
+    """All four layouts against numpy's float64 matmul of the explicit transposes."""
+    M, N, K = 37, 29, 53
+    X = _gen(M, K, 95, 0, "normal")
+    Y = _gen(K, N, 95, 1, "normal")
+    Cin = _gen(M, N, 95, 2, "uniform_pm1")
+    alpha, beta = -1.25, 0.375
+    ref = alpha * (X.astype(np.float64) @ Y.astype(np.float64)) + beta * Cin.astype(np.float64)
+    sref = (abs(alpha) * (np.abs(X).astype(np.float64) @ np.abs(Y).astype(np.float64)) +
+            abs(beta) * np.abs(Cin).astype(np.float64))
+    tol = 2 * (K + 2) * 2.0 ** -53 * sref
+    for ta in (False, True):
+        for tb in (False, True):
+            C, S = oracle.sgemm_ex(_stored(X, ta), _stored(Y, tb), ta, tb, alpha, beta, Cin,
+                                   lib=lib)
+            assert np.all(np.abs(C - ref) <= tol), (ta, tb)
+            assert np.all(np.abs(S - sref) <= tol), (ta, tb)
+            r = np.array([0, M - 1, 5, 17])
+            c = np.array([N - 1, 0, 3, 28])
+            Ce, Se = oracle.sgemm_ex(_stored(X, ta), _stored(Y, tb), ta, tb, alpha, beta, Cin,
+                                     rows=r, cols=c, lib=lib)
+            assert np.array_equal(Ce, C[r, c]) and np.array_equal(Se, S[r, c]), (ta, tb)
+
+
+def pin_ex_plain_form(lib):
+    """alpha = 1, beta = 0 with untransposed operands is the plain product, bitwise
+    (same k order), and a transposed store of the same operand gives the same bits."""
+    X = _gen(21, 33, 97, 0, "normal")
+    Y = _gen(33, 18, 97, 1, "normal")
+    C0, S0 = oracle.sgemm(X, Y, lib=lib)
+    zero_c = np.zeros((21, 18), dtype=np.float32)
+    for ta in (False, True):
+        for tb in (False, True):
+            C, S = oracle.sgemm_ex(_stored(X, ta), _stored(Y, tb), ta, tb, C=zero_c, lib=lib)
+            assert np.array_equal(C, C0) and np.array_equal(S, S0), (ta, tb)
+
+
+def pin_ex_closed_forms(lib):
+    """All-ones operands: C = alpha*K + beta*c exactly; beta == 0 never reads C (NaN
+    there stays out); alpha == 0 never reads A or B (NaN there stays out); a second
+    call with beta = -1 and C = the first result cancels to 0 on integer data."""
+    M, N, K = 6, 7, 12
+    ones_a, ones_b = synthgen.ones(M, K), synthgen.ones(K, N)
+    Cin = np.full((M, N), 3.0, dtype=np.float32)
+    C, S = oracle.sgemm_ex(ones_a, ones_b, alpha=2.0, beta=-0.5, C=Cin, lib=lib)
+    assert np.all(C == 2.0 * K - 1.5) and np.all(S == 2.0 * K + 1.5)
+    nan_c = np.full((M, N), np.nan, dtype=np.float32)
+    C, S = oracle.sgemm_ex(ones_a, ones_b, alpha=1.5, beta=0.0, C=nan_c, lib=lib)
+    assert np.all(C == 1.5 * K) and np.all(S == 1.5 * K)
+    nan_a = np.full((M, K), np.nan, dtype=np.float32)
+    nan_b = np.full((K, N), np.nan, dtype=np.float32)
+    C, S = oracle.sgemm_ex(nan_a, nan_b, alpha=0.0, beta=1.5, C=Cin, lib=lib)
+    assert np.all(C == 4.5) and np.all(S == 4.5)
+    A = _gen(M, K, 99, 0, "smallint")
+    B = _gen(K, N, 99, 1, "smallint")
+    P = (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float32)
+    C, _ = oracle.sgemm_ex(A, B, alpha=1.0, beta=-1.0, C=P, lib=lib)
+    assert np.all(C == 0.0)
+
+
 ALL_PINS = [pin_all_ones, pin_identity, pin_small_integers, pin_block_identity,
             pin_transpose, pin_brute_force, pin_library_fp64, pin_elements_match_full,
-            pin_leading_dimensions, pin_empty_sum]
+            pin_leading_dimensions, pin_empty_sum, pin_ex_brute_force, pin_ex_library_fp64,
+            pin_ex_plain_form, pin_ex_closed_forms]

@@ -16,14 +16,31 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "sgemm_oracle.c")
 MUTANTS = {
     "drop_last_term": ("for (int64_t k = 0; k < K; ++k) {", "for (int64_t k = 0; k < K - 1; ++k) {"),
     "skip_first_term": ("for (int64_t k = 0; k < K; ++k) {", "for (int64_t k = 1; k < K; ++k) {"),
-    "wrong_sign": ("c += a * b;", "c -= a * b;"),
+    "wrong_sign": ("\n        c += a * b;", "\n        c -= a * b;"),
     "transposed_B": ("double b = (double)B[k * ldb + j];", "double b = (double)B[j * ldb + k];"),
     "transposed_A": ("double a = (double)A[i * lda + k];", "double a = (double)A[k * lda + i];"),
     "a_index_uses_j": ("double a = (double)A[i * lda + k];", "double a = (double)A[j * lda + k];"),
-    "float_accumulator": ("double c = 0.0;", "float c = 0.0f;"),
-    "scale_without_abs": ("s += fabs(a) * fabs(b);", "s += a * b;"),
-    "nonzero_start": ("double c = 0.0;", "double c = 1e-300 + (K == 0);"),
+    "float_accumulator": ("\n    double c = 0.0;\n    double s = 0.0;\n    for",
+                          "\n    float c = 0.0f;\n    double s = 0.0;\n    for"),
+    "scale_without_abs": ("\n        s += fabs(a) * fabs(b);", "\n        s += a * b;"),
+    "nonzero_start": ("\n    double c = 0.0;\n    double s = 0.0;\n    for",
+                      "\n    double c = 1e-300 + (K == 0);\n    double s = 0.0;\n    for"),
     "b_uses_lda": ("double b = (double)B[k * ldb + j];", "double b = (double)B[k * lda + j];"),
+    # the general form
+    "ex_transa_ignored": ("p->transa ? (double)p->A[k * p->lda + i]",
+                          "p->transa ? (double)p->A[i * p->lda + k]"),
+    "ex_transb_ignored": ("p->transb ? (double)p->B[j * p->ldb + k]",
+                          "p->transb ? (double)p->B[k * p->ldb + j]"),
+    "ex_transb_reversed_k": ("p->transb ? (double)p->B[j * p->ldb + k]",
+                             "p->transb ? (double)p->B[j * p->ldb + (p->K - 1 - k)]"),
+    "ex_beta_read_when_zero": ("if (p->beta != 0.0) {", "if (1) {"),
+    "ex_alpha_zero_reads_ab": ("if (p->alpha != 0.0) {", "if (1) {"),
+    "ex_alpha_on_c": ("out += p->beta * cin;", "out += p->alpha * p->beta * cin;"),
+    "ex_beta_sign": ("out += p->beta * cin;", "out -= p->beta * cin;"),
+    "ex_scale_without_beta": ("scale += fabs(p->beta) * fabs(cin);", "scale += 0.0 * fabs(cin);"),
+    "ex_alpha_dropped": ("double out = p->alpha * c;", "double out = c;"),
+    "ex_wrong_sign": ("\n            c += a * b;", "\n            c -= a * b;"),
+    "ex_scale_without_abs": ("\n            s += fabs(a) * fabs(b);", "\n            s += a * b;"),
 }
 
 
