@@ -27,7 +27,9 @@ if ROOT not in sys.path:
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (matrix and vector), 2.4 GHz
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_mfma_8192_traffic.txt")
-KERNEL_SOURCES = ["dense_fp32_matrix_f32_amd/csrc/mfma.hip",
+KERNEL_SOURCES = ["dense_fp32_matrix_f32_amd/csrc/mfma_kernel.h",
+                  "dense_fp32_matrix_f32_amd/csrc/mfma_nn.hip",
+                  "dense_fp32_matrix_f32_amd/csrc/mfma.hip",
                   "dense_fp32_matrix_f32_amd/csrc/tile_order.h",
                   "dense_fp32_matrix_f32_amd/csrc/internal.h"]
 
@@ -98,25 +100,33 @@ def host_threads() -> int:
         return max(1, os.cpu_count() or 1)
 
 
-def make_inputs(torch, M, N, K, seed, dist="normal"):
+def make_inputs(torch, M, N, K, seed, dist="normal", layout=(0, 0)):
+    """Seeded host operands and their device copies.  With a transposed layout the
+    stored arrays are K x M (A) and N x K (B)."""
     import synthgen
-    A = synthgen.matrix(M, K, seed=seed, stream=0, dist=dist)
-    B = synthgen.matrix(K, N, seed=seed, stream=1, dist=dist)
+    ta, tb = layout
+    A = synthgen.matrix(K if ta else M, M if ta else K, seed=seed, stream=0, dist=dist)
+    B = synthgen.matrix(N if tb else K, K if tb else N, seed=seed, stream=1, dist=dist)
     dA = torch.from_numpy(A).cuda()
     dB = torch.from_numpy(B).cuda()
     dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
     return A, B, dA, dB, dC
 
 
-def time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warmup):
+def time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warmup, layout=(0, 0)):
     """Warm-up, then `steps` timed launches: wall clock between two full
     synchronisations, and per-launch HIP events on the launch stream."""
     stream = torch.cuda.current_stream()
-    lda, ldb, ldc = K, N, N
+    ta, tb = layout
+    lda, ldb, ldc = (M if ta else K), (K if tb else N), N
 
     def call():
-        st = sg.sgemm_f32_algo(M, N, K, dA.data_ptr(), lda, dB.data_ptr(), ldb, dC.data_ptr(), ldc,
-                               stream.cuda_stream, algo)
+        if layout == (0, 0):
+            st = sg.sgemm_f32_algo(M, N, K, dA.data_ptr(), lda, dB.data_ptr(), ldb,
+                                   dC.data_ptr(), ldc, stream.cuda_stream, algo)
+        else:
+            st = sg.sgemm_f32_ex_algo(ta, tb, M, N, K, 1.0, dA.data_ptr(), lda, dB.data_ptr(),
+                                      ldb, 0.0, dC.data_ptr(), ldc, stream.cuda_stream, algo)
         if st != 0:
             raise sg.SgemmError(st)
 
@@ -364,6 +374,9 @@ def main(argv=None):
     p.add_argument("--ladder", action="store_true",
                    help="time every algorithm of the ladder on --shape instead (one JSON line "
                         "per algorithm)")
+    p.add_argument("--layout", default="NN", choices=["NN", "NT", "TN", "TT"],
+                   help="storage order of A and B for the timed product (T: the operand is "
+                        "passed transposed through sgemm_f32_ex)")
     p.add_argument("--configs", action="store_true",
                    help="report every workload (512^3, 1024^3, 2048x3072x4096, 4095x4097x1023, "
                         "1x4096x4096, 8192^3) instead, one JSON line each")
@@ -410,13 +423,17 @@ def main(argv=None):
     algo = sg.ALGOS[args.algo]
     print(f"[bench] generating {M}x{K} and {K}x{N} N(0,1) inputs (seed {args.seed})",
           file=sys.stderr, flush=True)
-    A, B, dA, dB, dC = make_inputs(torch, M, N, K, args.seed)
+    layout = (int(args.layout[0] == "T"), int(args.layout[1] == "T"))
+    A, B, dA, dB, dC = make_inputs(torch, M, N, K, args.seed, layout=layout)
     chosen = sg.sgemm_f32_select(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N)
+    if layout != (0, 0):
+        chosen = sg.ALGO_MFMA
     used = chosen if algo == sg.ALGO_AUTO else algo
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up, algo "
           f"{sg.sgemm_f32_algo_name(used)}", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
-    wall, kms = time_product(torch, sg, M, N, K, dA, dB, dC, algo, args.steps, args.warmup)
+    wall, kms = time_product(torch, sg, M, N, K, dA, dB, dC, algo, args.steps, args.warmup,
+                             layout)
     flops = algorithmic_flops(M, N, K)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (wall / args.steps) / 1e12
@@ -437,12 +454,14 @@ def main(argv=None):
         "data": "synthetic",
         "pct_fp32_peak": round(100 * value / PEAK_FP32_TFLOPS, 2),
         "config": {"workload": f"C=A*B fp32 row-major M={M} N={N} K={K}, A,B iid N(0,1) "
-                               f"seed {args.seed}",
+                               f"seed {args.seed}" +
+                               ("" if layout == (0, 0) else f", operands {args.layout}"),
                    "M": M, "N": N, "K": K, "algo": sg.sgemm_f32_algo_name(used),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-                     "traffic": read_traffic() if (M, N, K) == (8192, 8192, 8192) else None,
+                     "traffic": read_traffic() if (M, N, K, layout) == (8192, 8192, 8192, (0, 0))
+                     else None,
                      "kernel_ms_avg": round(kavg, 4), "kernel_ms_min": round(min(kms), 4),
                      "algorithmic_flops": flops, "algorithmic_bytes": algorithmic_bytes(M, N, K),
                      "intensity_flop_per_byte": round(intensity(M, N, K), 2)},
@@ -472,7 +491,7 @@ def main(argv=None):
                        "kernel_ms_avg": round(k2avg, 4),
                        "pct_fp32_peak": round(100 * f2 / (k2avg * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 2)}
         del eA, eB, eC
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and layout == (0, 0):
         print(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr,
               flush=True)
         rec["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_seconds)

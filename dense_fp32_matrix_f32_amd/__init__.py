@@ -9,47 +9,67 @@ from __future__ import annotations
 
 from ._binding import (ALGO_AUTO, ALGO_COUNT, ALGO_LDS_TILED, ALGO_MFMA, ALGO_NAIVE,
                        ALGO_SKINNY, ALGO_SKINNY_N, ALGO_VALU_REGBLOCK, ALGOS, EXPORTED, LIB_PATH,
-                       SgemmError, lib, sgemm_f32, sgemm_f32_algo, sgemm_f32_algo_name,
-                       sgemm_f32_mfma_select, sgemm_f32_mfma_tile, sgemm_f32_mfma_tile_name,
-                       sgemm_f32_mfma_tiles, sgemm_f32_select)
+                       OP_N, OP_T, SgemmError, lib, sgemm_f32, sgemm_f32_algo, sgemm_f32_algo_name,
+                       sgemm_f32_colmajor, sgemm_f32_ex, sgemm_f32_ex_algo,
+                       sgemm_f32_ex_mfma_tile, sgemm_f32_mfma_select, sgemm_f32_mfma_tile,
+                       sgemm_f32_mfma_tile_name, sgemm_f32_mfma_tiles, sgemm_f32_select)
 
 __all__ = ["matmul", "sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name",
-           "sgemm_f32_mfma_tiles", "sgemm_f32_mfma_tile_name", "sgemm_f32_mfma_select",
-           "sgemm_f32_mfma_tile", "SgemmError", "ALGOS", "LIB_PATH", "EXPORTED", "lib"]
+           "sgemm_f32_ex", "sgemm_f32_ex_algo", "sgemm_f32_colmajor", "sgemm_f32_mfma_tiles",
+           "sgemm_f32_mfma_tile_name", "sgemm_f32_mfma_select", "sgemm_f32_mfma_tile",
+           "sgemm_f32_ex_mfma_tile", "SgemmError", "ALGOS", "LIB_PATH", "EXPORTED", "lib",
+           "OP_N", "OP_T"]
 
 
 def _operand(t, name):
+    """(pointer, leading dimension, transposed) of a 2-D float32 CUDA tensor that is
+    row-major (unit column stride) or the transpose of a row-major array (unit row
+    stride, e.g. ``X.t()``)."""
     import torch
     if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2:
         raise TypeError(f"{name} must be a 2-D float32 torch tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU")
-    if t.numel() > 0 and t.size(1) > 1 and t.stride(1) != 1:
-        raise ValueError(f"{name} needs unit column stride (row-major)")
-    ld = t.stride(0) if t.size(0) > 1 else t.size(1)
-    return t.data_ptr(), max(ld, t.size(1), 1)
+    rows, cols = t.shape
+    if t.numel() == 0 or cols <= 1 or t.stride(1) == 1:
+        ld = t.stride(0) if rows > 1 else cols
+        return t.data_ptr(), max(ld, cols, 1), False
+    if rows <= 1 or t.stride(0) == 1:
+        ld = t.stride(1)
+        return t.data_ptr(), max(ld, rows, 1), True
+    raise ValueError(f"{name} needs a unit stride in one dimension")
 
 
-def matmul(A, B, out=None, algo="auto", stream=None):
-    """Return C = A @ B for 2-D float32 CUDA tensors (row-major; views with a row
-    stride are passed as leading dimensions).  Enqueued on ``stream`` (default:
-    torch's current stream) without synchronising."""
+def matmul(A, B, out=None, algo="auto", stream=None, alpha=1.0, beta=0.0):
+    """Return C = alpha * A @ B + beta * out for 2-D float32 CUDA tensors.
+
+    Row-major tensors and views with a row stride are passed as they are;
+    transposed views (``X.t()``) are passed as transposed operands, without a
+    copy.  ``out`` must be row-major; it is read only when beta != 0 (a new
+    tensor is allocated when it is None, which needs beta == 0).  The product is
+    enqueued on ``stream`` (default: torch's current stream) without
+    synchronising."""
     import torch
-    pa, lda = _operand(A, "A")
-    pb, ldb = _operand(B, "B")
+    pa, lda, ta = _operand(A, "A")
+    pb, ldb, tb = _operand(B, "B")
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
     if out is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs out")
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     elif tuple(out.shape) != (M, N):
         raise ValueError("out has the wrong shape")
-    pc, ldc = _operand(out, "out")
+    pc, ldc, tc = _operand(out, "out")
+    if tc and M > 1 and N > 1:
+        raise ValueError("out must be row-major")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     algo_id = ALGOS[algo] if isinstance(algo, str) else int(algo)
     with torch.cuda.device(A.device):
-        st = sgemm_f32_algo(M, N, K, pa, lda, pb, ldb, pc, ldc, s.cuda_stream, algo_id)
+        st = sgemm_f32_ex_algo(int(ta), int(tb), M, N, K, float(alpha), pa, lda, pb, ldb,
+                               float(beta), pc, ldc, s.cuda_stream, algo_id)
     if st != 0:
         raise SgemmError(st)
     return out

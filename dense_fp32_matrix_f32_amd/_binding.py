@@ -27,9 +27,13 @@ ALGOS = {"auto": ALGO_AUTO, "naive": ALGO_NAIVE, "lds_tiled": ALGO_LDS_TILED,
 HIP_SUCCESS = 0
 HIP_ERROR_INVALID_VALUE = 1
 
+OP_N = 0
+OP_T = 1
+
 EXPORTED = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name",
+            "sgemm_f32_ex", "sgemm_f32_ex_algo", "sgemm_f32_colmajor",
             "sgemm_f32_mfma_tiles", "sgemm_f32_mfma_tile_name", "sgemm_f32_mfma_select",
-            "sgemm_f32_mfma_tile")
+            "sgemm_f32_mfma_tile", "sgemm_f32_ex_mfma_tile")
 
 _lib = None
 
@@ -74,6 +78,15 @@ def lib() -> ctypes.CDLL:
         l.sgemm_f32_mfma_select.restype = i
         l.sgemm_f32_mfma_tile.argtypes = args + [i]
         l.sgemm_f32_mfma_tile.restype = i
+        f = ctypes.c_float
+        ex_args = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp]
+        for name in ("sgemm_f32_ex", "sgemm_f32_colmajor"):
+            getattr(l, name).argtypes = ex_args
+            getattr(l, name).restype = i
+        l.sgemm_f32_ex_algo.argtypes = ex_args + [i]
+        l.sgemm_f32_ex_algo.restype = i
+        l.sgemm_f32_ex_mfma_tile.argtypes = ex_args + [i]
+        l.sgemm_f32_ex_mfma_tile.restype = i
         _lib = l
     return _lib
 
@@ -116,3 +129,30 @@ def sgemm_f32_mfma_select(M, N, K, compute_units=256) -> int:
 def sgemm_f32_mfma_tile(M, N, K, A, lda, B, ldb, C, ldc, stream=0, tile=0) -> int:
     """C = A·B on the matrix-core rung with configuration `tile`; returns the hipError_t."""
     return lib().sgemm_f32_mfma_tile(M, N, K, A, lda, B, ldb, C, ldc, stream, tile)
+
+
+def sgemm_f32_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    """C = alpha*op(A)*op(B) + beta*C (row-major); returns the hipError_t."""
+    return lib().sgemm_f32_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                              stream)
+
+
+def sgemm_f32_ex_algo(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,
+                      algo=ALGO_AUTO) -> int:
+    """As sgemm_f32_ex with a forced algorithm id; returns the hipError_t."""
+    return lib().sgemm_f32_ex_algo(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                   stream, algo)
+
+
+def sgemm_f32_colmajor(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                       stream=0) -> int:
+    """The general form with column-major arrays (reference-BLAS argument order)."""
+    return lib().sgemm_f32_colmajor(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                    stream)
+
+
+def sgemm_f32_ex_mfma_tile(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                           stream=0, tile=0) -> int:
+    """The general form on the matrix-core rung with configuration `tile`."""
+    return lib().sgemm_f32_ex_mfma_tile(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                        ldc, stream, tile)

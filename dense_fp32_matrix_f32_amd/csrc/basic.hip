@@ -1,31 +1,44 @@
-// basic.hip -- the first two rungs of the kernel ladder and the empty-sum fill.
+// basic.hip -- the first two rungs of the kernel ladder and the product-free
+// scaling of C.
 //
 // Rung 0 (naive) and rung 1 (LDS-tiled) are the two GPU designs that the pages
 // build: one thread per output element reading A and B straight from global
 // memory, then the same mapping with A and B staged tile by tile in on-chip
 // memory.  They are kept as reference points for the faster rungs and accept
-// every shape.
+// every shape and either storage order of each operand.
 #include "internal.h"
 
 namespace sgemm {
 
 // ---------------------------------------------------------------------------
-// K == 0: every C[i][j] is the empty sum, 0.
-__global__ __launch_bounds__(256) void zero_fill_kernel(int M, int N, float *__restrict__ C,
-                                                        int64_t ldc) {
+// No product (K == 0, the empty sum, or alpha == 0): C = beta*C, and C = 0
+// without reading it when beta == 0.
+__global__ __launch_bounds__(256) void scale_kernel(int M, int N, float *__restrict__ C,
+                                                    int64_t ldc, float beta) {
     const int64_t total = (int64_t)M * N;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
         const int64_t i = e / N, j = e - i * N;
-        C[i * ldc + j] = 0.0f;
+        float *c = C + i * ldc + j;
+        *c = beta == 0.0f ? 0.0f : beta * *c;
     }
 }
 
-hipError_t launch_zero_fill(const Problem &p, hipStream_t s) {
+hipError_t launch_scale(const Problem &p, hipStream_t s) {
     const int64_t total = (int64_t)p.M * p.N;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    return launch(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.M, p.N, p.C, p.ldc);
+    return launch(scale_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.M, p.N, p.C, p.ldc,
+                  p.beta);
+}
+
+// Element strides of op(A) (rows i, k) and op(B) (k, columns j).
+struct Strides {
+    int64_t ai, ak, bk, bj;
+};
+
+static Strides strides(const Problem &p) {
+    return {p.ta ? 1 : p.lda, p.ta ? p.lda : 1, p.tb ? 1 : p.ldb, p.tb ? p.ldb : 1};
 }
 
 // ---------------------------------------------------------------------------
@@ -38,17 +51,18 @@ hipError_t launch_zero_fill(const Problem &p, hipStream_t s) {
 constexpr int NAIVE_X = 64, NAIVE_Y = 4;
 
 __global__ __launch_bounds__(NAIVE_X *NAIVE_Y) void naive_kernel(
-    int M, int N, int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
-    int64_t ldb, float *__restrict__ C, int64_t ldc, int tiles_n) {
+    int M, int N, int K, const float *__restrict__ A, const float *__restrict__ B, Strides st,
+    float *__restrict__ C, int64_t ldc, float alpha, float beta, int tiles_n) {
     const int bn = blockIdx.x % tiles_n, bm = blockIdx.x / tiles_n;
     const int col = bn * NAIVE_X + threadIdx.x;
     const int row = bm * NAIVE_Y + threadIdx.y;
     if (row >= M || col >= N) return;
-    const float *a = A + (int64_t)row * lda;
-    const float *b = B + col;
+    const float *a = A + (int64_t)row * st.ai;
+    const float *b = B + (int64_t)col * st.bj;
     float sum = 0.0f;
-    for (int k = 0; k < K; ++k) sum = fmaf(a[k], b[(int64_t)k * ldb], sum);
-    C[(int64_t)row * ldc + col] = sum;
+    for (int k = 0; k < K; ++k) sum = fmaf(a[(int64_t)k * st.ak], b[(int64_t)k * st.bk], sum);
+    float *c = C + (int64_t)row * ldc + col;
+    *c = epilogue(sum, alpha, beta, c);
 }
 
 hipError_t launch_naive(const Problem &p, hipStream_t s) {
@@ -56,7 +70,7 @@ hipError_t launch_naive(const Problem &p, hipStream_t s) {
     const int64_t tiles_m = (p.M + NAIVE_Y - 1) / NAIVE_Y;
     if (tiles_n * tiles_m > INT32_MAX) return hipErrorInvalidValue;
     return launch(naive_kernel, dim3((unsigned)(tiles_n * tiles_m)), dim3(NAIVE_X, NAIVE_Y), 0, s,
-                  p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, (int)tiles_n);
+                  p.M, p.N, p.K, p.A, p.B, strides(p), p.C, p.ldc, p.alpha, p.beta, (int)tiles_n);
 }
 
 // ---------------------------------------------------------------------------
@@ -71,8 +85,8 @@ hipError_t launch_naive(const Problem &p, hipStream_t s) {
 constexpr int TILE = 16;
 
 __global__ __launch_bounds__(TILE *TILE) void lds_tiled_kernel(
-    int M, int N, int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
-    int64_t ldb, float *__restrict__ C, int64_t ldc, int tiles_n) {
+    int M, int N, int K, const float *__restrict__ A, const float *__restrict__ B, Strides st,
+    float *__restrict__ C, int64_t ldc, float alpha, float beta, int tiles_n) {
     __shared__ float As[TILE][TILE + 1];
     __shared__ float Bs[TILE][TILE + 1];
     const int tx = threadIdx.x, ty = threadIdx.y;
@@ -81,14 +95,17 @@ __global__ __launch_bounds__(TILE *TILE) void lds_tiled_kernel(
     float sum = 0.0f;
     for (int k0 = 0; k0 < K; k0 += TILE) {
         const int ka = k0 + tx, kb = k0 + ty;
-        As[ty][tx] = (row < M && ka < K) ? A[(int64_t)row * lda + ka] : 0.0f;
-        Bs[ty][tx] = (kb < K && col < N) ? B[(int64_t)kb * ldb + col] : 0.0f;
+        As[ty][tx] = (row < M && ka < K) ? A[(int64_t)row * st.ai + (int64_t)ka * st.ak] : 0.0f;
+        Bs[ty][tx] = (kb < K && col < N) ? B[(int64_t)kb * st.bk + (int64_t)col * st.bj] : 0.0f;
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < TILE; ++k) sum = fmaf(As[ty][k], Bs[k][tx], sum);
         __syncthreads();
     }
-    if (row < M && col < N) C[(int64_t)row * ldc + col] = sum;
+    if (row < M && col < N) {
+        float *c = C + (int64_t)row * ldc + col;
+        *c = epilogue(sum, alpha, beta, c);
+    }
 }
 
 hipError_t launch_lds_tiled(const Problem &p, hipStream_t s) {
@@ -96,7 +113,8 @@ hipError_t launch_lds_tiled(const Problem &p, hipStream_t s) {
     const int64_t tiles_m = (p.M + TILE - 1) / TILE;
     if (tiles_n * tiles_m > INT32_MAX) return hipErrorInvalidValue;
     return launch(lds_tiled_kernel, dim3((unsigned)(tiles_n * tiles_m)), dim3(TILE, TILE), 0, s,
-                  p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, (int)tiles_n);
+                  p.M, p.N, p.K, p.A, p.B, strides(p), p.C, p.ldc, p.alpha, p.beta,
+                  (int)tiles_n);
 }
 
 }  // namespace sgemm

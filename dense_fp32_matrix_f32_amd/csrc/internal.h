@@ -9,7 +9,10 @@
 
 namespace sgemm {
 
-// Validated arguments of one product C = A·B (row-major, element strides).
+// Validated arguments of one product C = alpha*op(A)*op(B) + beta*C (row-major,
+// element strides).  op(A) is A (M x K) or, with ta, the transpose of the K x M
+// array A; op(B) is B (K x N) or, with tb, the transpose of the N x K array B.
+// beta == 0 means C is not read.
 struct Problem {
     int M, N, K;
     const float *A;
@@ -18,7 +21,14 @@ struct Problem {
     int64_t ldb;
     float *C;
     int64_t ldc;
+    bool ta = false, tb = false;
+    float alpha = 1.0f, beta = 0.0f;
 };
+
+// alpha*acc, plus beta*C when beta != 0 (C is not read otherwise).
+__device__ __forceinline__ float epilogue(float acc, float alpha, float beta, const float *c) {
+    return beta == 0.0f ? alpha * acc : fmaf(beta, *c, alpha * acc);
+}
 
 // hipLaunchKernel with typed arguments; returns the launch status itself
 // rather than a sticky per-thread error.
@@ -33,7 +43,8 @@ inline hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_
     return pack(static_cast<Params>(args)...);
 }
 
-hipError_t launch_zero_fill(const Problem &p, hipStream_t s);
+// C = beta*C without a product (alpha == 0 or K == 0); beta == 0 writes zeros.
+hipError_t launch_scale(const Problem &p, hipStream_t s);
 hipError_t launch_naive(const Problem &p, hipStream_t s);
 hipError_t launch_lds_tiled(const Problem &p, hipStream_t s);
 hipError_t launch_valu_regblock(const Problem &p, hipStream_t s);

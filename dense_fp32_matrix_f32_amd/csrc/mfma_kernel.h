@@ -1,0 +1,678 @@
+// mfma_kernel.h -- register-blocked fp32 matrix-core kernel of the ladder, for
+// either storage order of each operand.
+//
+// Same decomposition as the pages' tiled kernel (page "CUDA算子优化(4)：矩阵乘法",
+// section "版本V1共享内存分块": each work-group owns a TILE_M x TILE_N block of C and
+// slides a TILE_K window along k, staging the A and B windows in on-chip memory),
+// re-sized for gfx950:
+//   * a BM x BN block of C per work-group, BK-wide k windows in a ring of two or
+//     three LDS stages (later windows are written while the current one is read,
+//     so one barrier per window replaces the pages' two);
+//   * global -> LDS copies as 16-byte loads, issued a window ahead into
+//     registers so that their latency overlaps a whole window of math;
+//   * the operand fragments of the next 8-wide k step are read from LDS while
+//     the MFMAs of the current step run; with three stages this reaches across
+//     the window boundary, so the barrier does not leave the matrix cores idle;
+//   * each wave owns a WM x WN sub-block held as (WM/32) x (WN/32) accumulators
+//     of v_mfma_f32_32x32x2f32 (full fp32 inputs, fp32 accumulation, 4096 flops
+//     per instruction), which is where the per-element fused multiply-adds of
+//     the pages' kernels go;
+//   * optionally KW groups of waves split each window's k range between them
+//     and add their partial blocks through LDS at the end, in a fixed order, so
+//     a small block of C still keeps all four SIMDs of a CU busy;
+//   * work-group ids are re-ordered so that each XCD works on one compact region
+//     of C (see tile_order.h).
+//
+// Operand storage.  op(A) is M x K and op(B) is K x N.  An operand is either
+// k-contiguous (A as given, or B transposed: rows of op(A), columns of op(B)
+// run along memory) or mn-contiguous (A transposed, or B as given).  Its window
+// is kept in LDS in the same orientation: a k-contiguous window as rows of BK
+// floats (pitch BK + PAD_A), an mn-contiguous one as BK rows of BM or BN floats
+// (pitch + PAD_B).  Both pitches keep the fragment reads below free of LDS bank
+// conflicts (64 banks; a 16-byte read serves 16 lanes per cycle).
+//
+// Operand placement.  The k order inside one MFMA is fixed by the hardware.
+// Across the four MFMAs of an 8-wide k step, lane half h supplies
+// k = k8 + 4h + q to the q-th instruction.
+//   * k-contiguous operand: a lane fetches the four consecutive k of its row
+//     (column) with one 16-byte LDS read per 32-wide accumulator block; MFMA row
+//     (column) r of block i is row (column) 32*i + r of the wave's strip.
+//   * mn-contiguous operand: MFMA row (column) r of block i stands for row
+//     (column) T*r + i of the wave's strip, T = WM/32 (WN/32), so a lane fetches
+//     its T adjacent rows (columns) for one k with one LDS access, and stores of
+//     C cover T adjacent columns at once.
+// A and B use the same k assignment, so every product opA[i][k]*opB[k][j] is
+// formed exactly once.
+//
+// Edges: rows and columns beyond M and N are read from the last valid one (they
+// only feed outputs that are not stored); the last, partial k window is
+// zero-filled on both operands (the pages' zero-fill of partial tiles), so no
+// value outside the logical matrices enters a stored result and no load leaves
+// the matrices' extents.
+#pragma once
+
+#include <cmath>
+#include <type_traits>
+
+#include "internal.h"
+
+namespace sgemm {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int N> struct VecOf;
+template <> struct VecOf<1> { typedef float type; };
+template <> struct VecOf<2> { typedef f32x2 type; };
+template <> struct VecOf<4> { typedef f32x4 type; };
+// Three adjacent floats, 4-byte aligned: read from LDS as a two-dword and a
+// one-dword access.
+struct F3 {
+    float e[3];
+};
+template <> struct VecOf<3> { typedef F3 type; };
+
+template <int N>
+__device__ __forceinline__ float lane_of(const typename VecOf<N>::type &v, int j) {
+    if constexpr (N == 1) {
+        return v;
+    } else if constexpr (N == 3) {
+        return v.e[j];
+    } else {
+        return v[j];
+    }
+}
+
+// LDS accesses needed to read N adjacent floats of one row.
+constexpr int lds_reads(int n) { return n == 3 ? 2 : 1; }
+
+// 16-byte load from a 4-byte aligned address (gfx950 global memory instructions
+// accept dword-aligned multi-dword accesses).
+__device__ __forceinline__ f32x4 load16(const float *p) {
+    f32x4 v;
+    __builtin_memcpy(&v, p, 16);
+    return v;
+}
+
+// Scheduling hint for one basic block holding MF MFMAs, DSR LDS reads, DSW LDS
+// writes and VMR global loads: each memory instruction is placed right after an
+// MFMA, so a single wave keeps its matrix core fed while it issues them.  When
+// there are fewer MFMAs than memory instructions the block is left to the
+// default scheduler.
+template <int MF, int DSR, int DSW, int VMR>
+__device__ __forceinline__ void interleave() {
+    if constexpr (MF >= DSR + DSW + VMR) {
+#pragma unroll
+        for (int i = 0; i < DSR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        }
+#pragma unroll
+        for (int i = 0; i < DSW; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        }
+#pragma unroll
+        for (int i = 0; i < VMR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+        }
+        if constexpr (MF > DSR + DSW + VMR)
+            __builtin_amdgcn_sched_group_barrier(0x008, MF - DSR - DSW - VMR, 0);
+    }
+}
+
+// BM x BN block of C per work-group, BK-wide k windows, WM x WN block per wave,
+// KW wave groups splitting k, GROUP_M tile-rows per ordering group, STAGES LDS
+// buffers (2 or 3), OCC the number of waves per SIMD that the register
+// allocation must allow, PAD_A / PAD_B the LDS row padding of k-contiguous and
+// mn-contiguous windows.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int KW_, int GROUP_M_, int STAGES_ = 2,
+          int OCC_ = 1, int PAD_A_ = 4, int PAD_B_ = 8>
+struct MfmaTile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, KW = KW_;
+    static constexpr int GROUP_M = GROUP_M_, STAGES = STAGES_, OCC = OCC_;
+    static constexpr int PAD_A = PAD_A_, PAD_B = PAD_B_;
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int SPATIAL = WAVES_M * WAVES_N;    // waves per k group
+    static constexpr int THREADS = SPATIAL * KW * 64;
+    static constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 accumulators per wave
+    static constexpr int ACC = TM * TN * 16;             // accumulator floats per lane
+    static constexpr int RED = (KW - 1) * SPATIAL * 64 * ACC;  // split-k partials
+    static constexpr int A_TOTAL = BM * BK / 4, B_TOTAL = BK * BN / 4;  // 16-byte vectors
+    static constexpr int A_VECS = (A_TOTAL + THREADS - 1) / THREADS;     // per thread
+    static constexpr int B_VECS = (B_TOTAL + THREADS - 1) / THREADS;
+    static constexpr int STEPS = BK / (8 * KW);          // 8-wide k steps per group per window
+    static constexpr int MF = 4 * TM * TN;               // MFMAs per step
+    static constexpr int DSW = A_VECS + B_VECS;          // LDS writes per window
+    static constexpr int VMR = A_VECS + B_VECS;          // global loads per window
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tiling");
+    static_assert(TM >= 1 && TM <= 4 && TN >= 1 && TN <= 4,
+                  "a lane holds 1 to 4 adjacent rows or columns");
+    static_assert(BK % (8 * KW) == 0 && BK % 4 == 0, "k window splits into 8-wide steps");
+    static_assert(BM % 4 == 0 && BN % 4 == 0, "16-byte vectors along m and n");
+    static_assert(THREADS <= 1024, "work-group size");
+    static_assert(PAD_A_ % 4 == 0 && PAD_B_ % 4 == 0, "16-byte aligned LDS rows");
+    static_assert(STAGES == 2 || (STAGES == 3 && STEPS % 2 == 0),
+                  "a three-stage ring carries fragments across windows in an even step count");
+};
+
+// A tile configuration with the storage order of each operand: TA (op(A) is the
+// transpose of the stored K x M array) and TB (op(B) is the transpose of the
+// stored N x K array).
+template <class T, bool TA_, bool TB_>
+struct Cfg : T {
+    static constexpr bool TA = TA_, TB = TB_;
+    static constexpr int PA = TA ? T::BM + T::PAD_B : T::BK + T::PAD_A;  // A window pitch
+    static constexpr int PB = TB ? T::BK + T::PAD_A : T::BN + T::PAD_B;  // B window pitch
+    static constexpr int A_STAGE = (TA ? T::BK : T::BM) * PA;
+    static constexpr int B_STAGE = (TB ? T::BN : T::BK) * PB;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int LDS_FLOATS = T::STAGES * STAGE > T::RED ? T::STAGES * STAGE : T::RED;
+    static constexpr int DSR_A = TA ? 4 * lds_reads(T::TM) : T::TM;  // LDS reads per step
+    static constexpr int DSR_B = TB ? T::TN : 4 * lds_reads(T::TN);
+    static constexpr int DSR = DSR_A + DSR_B;
+    // The steady-state loop writes LDS in the first step of a window and issues
+    // the `vmr` global loads of a later window in the same step, or in the second
+    // step when one step has too few MFMAs to cover all of those memory
+    // instructions.
+    static constexpr int load_step(int vmr) {
+        return (T::STEPS > 1 && T::MF < DSR + T::DSW + vmr) ? 1 : 0;
+    }
+    static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
+};
+
+// The operands of one product C = alpha*op(A)*op(B) + beta*C.
+struct GemmArgs {
+    int M, N, K;
+    const float *__restrict__ A;
+    int64_t lda;
+    const float *__restrict__ B;
+    int64_t ldb;
+    float *__restrict__ C;
+    int64_t ldc;
+    float alpha, beta;
+};
+
+template <class T>
+using Acc = f32x16[T::TM][T::TN];
+
+// Global -> register -> LDS copy of one operand's k window, for the `VECS`
+// 16-byte vectors this work-item owns (vector v exists iff tid + v*THREADS <
+// TOTAL; a missing one re-reads the last vector and is not stored).
+//   k-contiguous (KC): ROWS rows (of op(A) or columns of op(B)) of BK floats;
+//     rows beyond `extent` read the last valid one.
+//   mn-contiguous: BK rows of COLS floats (along m or n); columns beyond
+//     `extent` read the last valid one.
+template <class T, bool KC, int ROWS_OR_COLS, int TOTAL, int VECS>
+struct Operand {
+    static constexpr int Q = KC ? T::BK / 4 : ROWS_OR_COLS / 4;  // vectors per LDS row
+    const float *src[VECS];
+    int lds[VECS];
+    int kofs[VECS];  // KC: k offset of the vector in the window; else its k row
+    int pos[VECS];   // mn-contiguous: first column (m or n) of the vector
+    f32x4 r[VECS];
+
+    __device__ __forceinline__ static bool has(int tid, int v) {
+        return (TOTAL % T::THREADS == 0) || tid + v * T::THREADS < TOTAL;
+    }
+
+    // origin: first row (KC) or column of the block; extent: M or N; ld: row
+    // stride of the stored array; base/pitch: LDS placement of the window.
+    __device__ __forceinline__ void init(const float *X, int64_t ld, int origin, int extent,
+                                         int base, int pitch, int tid) {
+#pragma unroll
+        for (int v = 0; v < VECS; ++v) {
+            const int c = min(tid + v * T::THREADS, TOTAL - 1);
+            const int row = c / Q, q = c % Q;
+            if constexpr (KC) {
+                const int gr = min(origin + row, extent - 1);
+                src[v] = X + (int64_t)gr * ld + q * 4;
+                kofs[v] = q * 4;
+                pos[v] = 0;
+            } else {
+                src[v] = X + (int64_t)row * ld + origin + q * 4;
+                kofs[v] = row;
+                pos[v] = origin + q * 4;
+            }
+            lds[v] = base + row * pitch + q * 4;
+        }
+    }
+
+    // Full window at k0 (every k < K).  INSIDE: every column of an mn-contiguous
+    // block lies inside its matrix, so whole 16-byte vectors are read.
+    template <bool INSIDE>
+    __device__ __forceinline__ void fetch_full(int64_t k0, int64_t ld, int extent) {
+#pragma unroll
+        for (int v = 0; v < VECS; ++v) {
+            if constexpr (KC) {
+                r[v] = load16(src[v] + k0);
+            } else if constexpr (INSIDE) {
+                r[v] = load16(src[v] + k0 * ld);
+            } else {
+                const float *row = src[v] + k0 * ld - pos[v];
+                r[v].x = row[min(pos[v] + 0, extent - 1)];
+                r[v].y = row[min(pos[v] + 1, extent - 1)];
+                r[v].z = row[min(pos[v] + 2, extent - 1)];
+                r[v].w = row[min(pos[v] + 3, extent - 1)];
+            }
+        }
+    }
+
+    // Any window: the general form of fetch_full, zeroing every element with k >= K.
+    __device__ __forceinline__ void fetch(int64_t k0, int64_t ld, int extent, int K,
+                                          bool inside) {
+        if (k0 + T::BK <= K) {
+            if (inside) {
+                fetch_full<true>(k0, ld, extent);
+            } else {
+                fetch_full<false>(k0, ld, extent);
+            }
+            return;
+        }
+#pragma unroll
+        for (int v = 0; v < VECS; ++v) {
+            if constexpr (KC) {
+                const int64_t kv = K - (k0 + kofs[v]);
+                const float *p = src[v] + k0;
+                r[v].x = kv > 0 ? p[0] : 0.0f;
+                r[v].y = kv > 1 ? p[1] : 0.0f;
+                r[v].z = kv > 2 ? p[2] : 0.0f;
+                r[v].w = kv > 3 ? p[3] : 0.0f;
+            } else {
+                if (k0 + kofs[v] < K) {
+                    const float *row = src[v] + k0 * ld - pos[v];
+                    r[v].x = row[min(pos[v] + 0, extent - 1)];
+                    r[v].y = row[min(pos[v] + 1, extent - 1)];
+                    r[v].z = row[min(pos[v] + 2, extent - 1)];
+                    r[v].w = row[min(pos[v] + 3, extent - 1)];
+                } else {
+                    r[v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void stash(float *stage, int tid) const {
+#pragma unroll
+        for (int v = 0; v < VECS; ++v)
+            if (has(tid, v)) *(f32x4 *)(stage + lds[v]) = r[v];
+    }
+};
+
+// acc += the product of op(A) rows m0..m0+BM-1 and op(B) columns n0..n0+BN-1
+// over the k windows [w_begin, w_end) (window w covers k = w*BK .. w*BK+BK-1).
+// Called by every work-item of the group; uses all of `lds` and ends on a
+// barrier, so LDS is free again when it returns.
+template <class C>
+__device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, int n0,
+                                         int w_begin, int w_end, Acc<C> &acc) {
+    typedef typename VecOf<C::TM>::type AVec;
+    typedef typename VecOf<C::TN>::type BVec;
+    const int M = g.M, N = g.N, K = g.K;
+    const int64_t lda = g.lda, ldb = g.ldb;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int kg = wave / C::SPATIAL, sw = wave % C::SPATIAL;
+    const int wm = sw / C::WAVES_N, wn = sw % C::WAVES_N;
+
+    Operand<C, !C::TA, C::BM, C::A_TOTAL, C::A_VECS> a;
+    Operand<C, C::TB, C::BN, C::B_TOTAL, C::B_VECS> b;
+    a.init(g.A, lda, m0, M, 0, C::PA, tid);
+    b.init(g.B, ldb, n0, N, C::A_STAGE, C::PB, tid);
+    // mn-contiguous blocks that reach past their matrix read clamped columns
+    const bool a_inside = !C::TA || m0 + C::BM <= M;
+    const bool b_inside = C::TB || n0 + C::BN <= N;
+    const bool interior = a_inside && b_inside;
+
+    auto fetch = [&](int64_t k0) {
+        a.fetch(k0, lda, M, K, a_inside);
+        b.fetch(k0, ldb, N, K, b_inside);
+    };
+    auto stash = [&](int stage) {
+        float *s = lds + stage * C::STAGE;
+        a.stash(s, tid);
+        b.stash(s, tid);
+    };
+
+    // Fragment placement (see the header comment).
+    const int a_frag = C::TA ? (4 * lh) * C::PA + wm * C::WM + C::TM * lr
+                             : (wm * C::WM + lr) * C::PA + 4 * lh;
+    const int b_frag = C::A_STAGE + (C::TB ? (wn * C::WN + lr) * C::PB + 4 * lh
+                                           : (4 * lh) * C::PB + wn * C::WN + C::TN * lr);
+
+    // Fragments of one 8-wide k step.
+    struct Frag {
+        typename std::conditional<C::TA, AVec[4], f32x4[C::TM]>::type a;
+        typename std::conditional<C::TB, f32x4[C::TN], BVec[4]>::type b;
+    };
+    auto read_frag = [&](Frag &f, const float *s, int t) {
+        const int k8 = (t * C::KW + kg) * 8;
+        if constexpr (C::TA) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) f.a[q] = *(const AVec *)(s + a_frag + (k8 + q) * C::PA);
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+                f.a[i] = *(const f32x4 *)(s + a_frag + i * 32 * C::PA + k8);
+        }
+        if constexpr (C::TB) {
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+                f.b[j] = *(const f32x4 *)(s + b_frag + j * 32 * C::PB + k8);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) f.b[q] = *(const BVec *)(s + b_frag + (k8 + q) * C::PB);
+        }
+    };
+    auto multiply = [&](const Frag &f) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) {
+                    float av, bv;
+                    if constexpr (C::TA) {
+                        av = lane_of<C::TM>(f.a[q], i);
+                    } else {
+                        av = f.a[i][q];
+                    }
+                    if constexpr (C::TB) {
+                        bv = f.b[j][q];
+                    } else {
+                        bv = lane_of<C::TN>(f.b[q], j);
+                    }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[i][j], 0, 0, 0);
+                }
+    };
+
+    // Prologue: the first STAGES-1 windows go to LDS, the next one to registers.
+    fetch((int64_t)w_begin * C::BK);
+    stash(0);
+    if constexpr (C::STAGES == 3) {
+        if (w_begin + 1 < w_end) {
+            fetch((int64_t)(w_begin + 1) * C::BK);
+            stash(1);
+        }
+    }
+    __syncthreads();
+    if (w_begin + C::STAGES - 1 < w_end) fetch((int64_t)(w_begin + C::STAGES - 1) * C::BK);
+
+    Frag frag[2];
+    int cur = 0;  // LDS stage of window w
+    int w = w_begin;
+    if constexpr (C::STAGES == 3) read_frag(frag[0], lds, 0);
+
+    // Steady state: a window whose successors up to w + STAGES are all full.
+    // The body has no branches, so the copies of later windows (LDS stores of
+    // window w + STAGES - 1, global loads of window w + STAGES) and the fragment
+    // reads of the next step are spread one by one between the MFMAs instead of
+    // stalling the matrix cores in a block of their own.  Work-groups whose
+    // block reaches past M or N on an mn-contiguous operand (EDGE) load that
+    // operand one element at a time with the index clamped, which keeps the
+    // body free of branches there too.
+    auto steady = [&](auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        constexpr int VMR = EDGE ? (C::TA ? 4 : 1) * C::A_VECS + (C::TB ? 1 : 4) * C::B_VECS
+                                 : C::VMR;
+        constexpr int LOAD_STEP = C::load_step(VMR);
+        const int steady_end = min(w_end, K / C::BK) - C::STAGES;
+        for (; w < steady_end; ++w) {
+            const float *s = lds + cur * C::STAGE;
+            const int next = cur + 1 == C::STAGES ? 0 : cur + 1;
+            const int fill = cur == 0 ? C::STAGES - 1 : cur - 1;
+            if constexpr (C::STAGES == 2) read_frag(frag[0], s, 0);
+#pragma unroll
+            for (int t = 0; t < C::STEPS; ++t) {
+                if (t + 1 < C::STEPS) {
+                    read_frag(frag[(t + 1) & 1], s, t + 1);
+                } else if constexpr (C::STAGES == 3) {
+                    read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
+                }
+                if (t == 0) stash(fill);
+                if (t == LOAD_STEP) {
+                    const int64_t k0 = (int64_t)(w + C::STAGES) * C::BK;
+                    a.template fetch_full<!EDGE>(k0, lda, M);
+                    b.template fetch_full<!EDGE>(k0, ldb, N);
+                }
+                multiply(frag[t & 1]);
+                // LDS reads issued in step 0, in a middle step and in the last step.
+                constexpr int R0 = (1 < C::STEPS || C::STAGES == 3) ? C::DSR : 0;
+                constexpr int RL = C::STAGES == 3 ? C::DSR : 0;
+                constexpr int R1 = 2 < C::STEPS ? C::DSR : RL;
+                constexpr int VM0 = LOAD_STEP == 0 ? VMR : 0;
+                if (t == 0) {
+                    interleave<C::MF, R0, C::DSW, VM0>();
+                } else if (t == LOAD_STEP) {
+                    interleave<C::MF, R1, 0, VMR>();
+                } else if (t + 1 < C::STEPS) {
+                    interleave<C::MF, C::DSR, 0, 0>();
+                } else {
+                    interleave<C::MF, RL, 0, 0>();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();
+            cur = next;
+        }
+    };
+    if (interior) {
+        steady(std::false_type{});
+    } else {
+        steady(std::true_type{});
+    }
+
+    // Remaining windows (the last STAGES ones and a partial last window): the
+    // same schedule with the copies guarded.
+    for (; w < w_end; ++w) {
+        const float *s = lds + cur * C::STAGE;
+        const int next = cur + 1 == C::STAGES ? 0 : cur + 1;
+        if constexpr (C::STAGES == 2) read_frag(frag[0], s, 0);
+#pragma unroll
+        for (int t = 0; t < C::STEPS; ++t) {
+            // Issue the reads of the following step before this step's MFMAs.  After
+            // the last window the cross-window read fetches an unused stage; keeping
+            // it unconditional lets the LDS wait counts stay exact.
+            if (t + 1 < C::STEPS) {
+                read_frag(frag[(t + 1) & 1], s, t + 1);
+            } else if constexpr (C::STAGES == 3) {
+                read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            multiply(frag[t & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Window w + STAGES - 1 goes from registers to the stage freed by window w - 1,
+        // and the loads of the window after it are issued.
+        if (w + C::STAGES - 1 < w_end) {
+            const int fill = cur == 0 ? C::STAGES - 1 : cur - 1;
+            stash(fill);
+            if (w + C::STAGES < w_end) fetch((int64_t)(w + C::STAGES) * C::BK);
+        }
+        __syncthreads();
+        cur = next;
+    }
+}
+
+// Store the accumulators of block (m0, n0) to C; rows >= M and columns >= N are
+// skipped.  Accumulator r of block (i, j) holds MFMA row rho = 8*(r/4) + 4*lh +
+// r%4 and MFMA column lr of that block, placed as described in the header.
+template <class C>
+__device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, const Acc<C> &acc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int sw = wave % C::SPATIAL;
+    const int wm = sw / C::WAVES_N, wn = sw % C::WAVES_N;
+    const int M = g.M, N = g.N;
+    float *__restrict__ Cm = g.C;
+    const int64_t ldc = g.ldc;
+    const float alpha = g.alpha, beta = g.beta;
+    const bool full = (m0 + C::BM <= M) && (n0 + C::BN <= N);
+    const int strip_m = m0 + wm * C::WM, strip_n = n0 + wn * C::WN;
+    auto row_of = [&](int i, int r) {
+        const int rho = 8 * (r >> 2) + 4 * lh + (r & 3);
+        return strip_m + (C::TA ? C::TM * rho + i : 32 * i + rho);
+    };
+    // mn-contiguous B: a lane's TN adjacent columns; k-contiguous B: one column per block
+    const int col0 = strip_n + (C::TB ? lr : C::TN * lr);
+    auto col_of = [&](int j) { return col0 + (C::TB ? 32 * j : j); };
+    auto put = [&](float *dst, float v) { *dst = epilogue(v, alpha, beta, dst); };
+    if (full) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float *dst = Cm + (int64_t)row_of(i, r) * ldc;
+                if constexpr (!C::TB) {
+                    float v[C::TN];
+                    if (beta == 0.0f) {
+#pragma unroll
+                        for (int j = 0; j < C::TN; ++j) v[j] = alpha * acc[i][j][r];
+                    } else {
+                        float old[C::TN];
+                        __builtin_memcpy(old, dst + col0, sizeof(old));
+#pragma unroll
+                        for (int j = 0; j < C::TN; ++j) v[j] = fmaf(beta, old[j], alpha * acc[i][j][r]);
+                    }
+                    __builtin_memcpy(dst + col0, v, sizeof(v));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j) put(dst + col_of(j), acc[i][j][r]);
+                }
+            }
+            // one row block at a time keeps few accumulators in flight
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row_of(i, r);
+                if (row < M) {
+                    float *dst = Cm + (int64_t)row * ldc;
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j)
+                        if (col_of(j) < N) put(dst + col_of(j), acc[i][j][r]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Split-k inside the work-group: groups 1..KW-1 hand their partial blocks to
+// group 0 through LDS, which adds them in group order.  Returns true for the
+// waves that hold the finished block.
+template <class C>
+__device__ __forceinline__ bool kw_reduce(float *lds, Acc<C> &acc) {
+    if constexpr (C::KW == 1) {
+        return true;
+    } else {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int kg = wave / C::SPATIAL, sw = wave % C::SPATIAL;
+        float *red = lds + sw * 64 * C::ACC + lane;
+        constexpr int GROUP_STRIDE = C::SPATIAL * 64 * C::ACC;
+        if (kg > 0) {
+            float *dst = red + (kg - 1) * GROUP_STRIDE;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dst[((i * C::TN + j) * 16 + r) * 64] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (kg > 0) return false;
+#pragma unroll
+        for (int gi = 1; gi < C::KW; ++gi) {
+            const float *src = red + (gi - 1) * GROUP_STRIDE;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[i][j][r] += src[((i * C::TN + j) * 16 + r) * 64];
+        }
+        return true;
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void zero_acc(Acc<C> &acc) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
+}
+
+// Data-parallel form: one work-group per BM x BN block of C.
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_kernel(GemmArgs g, int tiles_m,
+                                                                 int tiles_n) {
+    __shared__ __attribute__((aligned(16))) float lds[C::LDS_FLOATS];
+    int tm, tn;
+    tile_order(blockIdx.x, tiles_m, tiles_n, C::GROUP_M, &tm, &tn);
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    Acc<C> acc;
+    zero_acc<C>(acc);
+    mma_tile<C>(g, lds, m0, n0, 0, (g.K + C::BK - 1) / C::BK, acc);
+    if (!kw_reduce<C>(lds, acc)) return;
+    store_tile<C>(g, m0, n0, acc);
+}
+
+template <class T, bool TA, bool TB>
+hipError_t launch_tile(const Problem &p, hipStream_t s) {
+    using C = Cfg<T, TA, TB>;
+    const int64_t tiles_m = (p.M + C::BM - 1) / C::BM;
+    const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
+    if (tiles_m * tiles_n > INT32_MAX) return hipErrorInvalidValue;
+    const GemmArgs g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
+    return launch(mfma_kernel<C>, dim3((unsigned)(tiles_m * tiles_n)), dim3(C::THREADS), 0, s, g,
+                  (int)tiles_m, (int)tiles_n);
+}
+
+// ---------------------------------------------------------------------------
+// Tile configurations.
+// 256 x 256 blocks, one wave per SIMD with 128 x 128 of C each: large products.
+using TileHuge = MfmaTile<256, 256, 16, 128, 128, 1, 8, 3>;
+using TileWide = MfmaTile<128, 128, 16, 32, 128, 1, 8, 3>;
+// 128 x 192 blocks of 64 x 96 per wave, k split over two wave groups (two waves
+// per SIMD): one block per CU on grids of about 256 blocks, such as 2048 x 3072.
+using TileSplit192 = MfmaTile<128, 192, 32, 64, 96, 2, 8, 3>;
+// 192 x 128 blocks of 96 x 64 per wave.
+using TileTall = MfmaTile<192, 128, 16, 96, 64, 1, 8, 3>;
+using TileSmall = MfmaTile<64, 64, 16, 32, 32, 1, 4, 3>;
+using TileSplit64 = MfmaTile<64, 64, 32, 32, 32, 2, 4, 3>;
+// k split four ways: one 8-wide step per group and window, so two stages.
+using TileTiny = MfmaTile<32, 32, 32, 32, 32, 4, 4, 2>;
+
+constexpr int kTileCount = 7;
+
+// Launch configuration `tile` (0 <= tile < kTileCount, in the order above) for
+// one storage order (defined in mfma_nn.hip, mfma_nt.hip, mfma_tn.hip, mfma_tt.hip).
+hipError_t launch_mfma_nn(const Problem &p, hipStream_t s, int tile);
+hipError_t launch_mfma_nt(const Problem &p, hipStream_t s, int tile);
+hipError_t launch_mfma_tn(const Problem &p, hipStream_t s, int tile);
+hipError_t launch_mfma_tt(const Problem &p, hipStream_t s, int tile);
+
+#define SGEMM_MFMA_LAUNCHER(NAME, TA, TB)                                                     \
+    hipError_t NAME(const Problem &p, hipStream_t s, int tile) {                             \
+        switch (tile) {                                                                       \
+        case 0: return launch_tile<TileHuge, TA, TB>(p, s);                                   \
+        case 1: return launch_tile<TileWide, TA, TB>(p, s);                                   \
+        case 2: return launch_tile<TileSplit192, TA, TB>(p, s);                               \
+        case 3: return launch_tile<TileTall, TA, TB>(p, s);                                   \
+        case 4: return launch_tile<TileSmall, TA, TB>(p, s);                                  \
+        case 5: return launch_tile<TileSplit64, TA, TB>(p, s);                                \
+        case 6: return launch_tile<TileTiny, TA, TB>(p, s);                                   \
+        default: return hipErrorInvalidValue;                                                 \
+        }                                                                                     \
+    }
+
+}  // namespace sgemm

@@ -8,7 +8,7 @@ using sgemm::Problem;
 
 namespace {
 
-// Byte extent [lo, hi) of a rows x cols row-major operand with row stride ld.
+// Byte extent [lo, hi) of a rows x cols row-major array with row stride ld.
 struct Extent {
     uintptr_t lo, hi;
 };
@@ -20,29 +20,71 @@ Extent extent(const void *p, int64_t rows, int64_t cols, int64_t ld) {
 
 bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// hipSuccess if the arguments are a valid product, else hipErrorInvalidValue.
-hipError_t validate(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-                    const float *C, int ldc) {
+int at_least_one(int x) { return x > 1 ? x : 1; }
+
+// hipSuccess if the arguments describe a valid C = alpha*op(A)*op(B) + beta*C,
+// else hipErrorInvalidValue.  A and B are read only when alpha != 0 and K > 0.
+hipError_t validate(int transa, int transb, int M, int N, int K, float alpha, const float *A,
+                    int lda, const float *B, int ldb, const float *C, int ldc) {
+    if ((transa != SGEMM_F32_OP_N && transa != SGEMM_F32_OP_T) ||
+        (transb != SGEMM_F32_OP_N && transb != SGEMM_F32_OP_T))
+        return hipErrorInvalidValue;
     if (M < 0 || N < 0 || K < 0) return hipErrorInvalidValue;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    if (lda < at_least_one(transa ? M : K) || ldb < at_least_one(transb ? K : N) ||
+        ldc < at_least_one(N))
         return hipErrorInvalidValue;
     if (M == 0 || N == 0) return hipSuccess;
     if (C == nullptr) return hipErrorInvalidValue;
-    if (K == 0) return hipSuccess;
+    if (K == 0 || alpha == 0.0f) return hipSuccess;
     if (A == nullptr || B == nullptr) return hipErrorInvalidValue;
     const Extent c = extent(C, M, N, ldc);
-    if (overlaps(c, extent(A, M, K, lda)) || overlaps(c, extent(B, K, N, ldb)))
-        return hipErrorInvalidValue;
+    const Extent a = transa ? extent(A, K, M, lda) : extent(A, M, K, lda);
+    const Extent b = transb ? extent(B, N, K, ldb) : extent(B, K, N, ldb);
+    if (overlaps(c, a) || overlaps(c, b)) return hipErrorInvalidValue;
     return hipSuccess;
 }
 
-// Few rows or few columns: the product streams one operand and is bound by
-// memory, so the streaming kernels win; everything else goes to matrix cores.
-int choose(int M, int N, int K) {
+// Untransposed products with few rows or few columns stream one operand and are
+// bound by memory, so the streaming kernels win; everything else goes to the
+// matrix cores.
+int choose(int transa, int transb, int M, int N, int K) {
     (void)K;
-    if (M <= 8) return SGEMM_F32_ALGO_SKINNY;
-    if (N <= 8) return SGEMM_F32_ALGO_SKINNY_N;
+    if (transa == SGEMM_F32_OP_N && transb == SGEMM_F32_OP_N) {
+        if (M <= 8) return SGEMM_F32_ALGO_SKINNY;
+        if (N <= 8) return SGEMM_F32_ALGO_SKINNY_N;
+    }
     return SGEMM_F32_ALGO_MFMA;
+}
+
+bool handles_transposes(int algo) {
+    return algo == SGEMM_F32_ALGO_AUTO || algo == SGEMM_F32_ALGO_NAIVE ||
+           algo == SGEMM_F32_ALGO_LDS_TILED || algo == SGEMM_F32_ALGO_MFMA;
+}
+
+Problem problem(int transa, int transb, int M, int N, int K, float alpha, const float *A,
+                int lda, const float *B, int ldb, float beta, float *C, int ldc) {
+    Problem p{M, N, K, A, lda, B, ldb, C, ldc};
+    p.ta = transa == SGEMM_F32_OP_T;
+    p.tb = transb == SGEMM_F32_OP_T;
+    p.alpha = alpha;
+    p.beta = beta;
+    return p;
+}
+
+// Validation and the product-free cases shared by the entry points.  Returns
+// true with *status set when nothing is left to launch.
+bool trivial(int transa, int transb, int M, int N, int K, float alpha, const float *A, int lda,
+             const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream,
+             hipError_t *status) {
+    *status = validate(transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (*status != hipSuccess) return true;
+    if (M == 0 || N == 0) return true;
+    if (K == 0 || alpha == 0.0f) {
+        *status = sgemm::launch_scale(
+            problem(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), stream);
+        return true;
+    }
+    return false;
 }
 
 }  // namespace
@@ -62,20 +104,24 @@ extern "C" const char *sgemm_f32_algo_name(int algo) {
 
 extern "C" int sgemm_f32_select(int M, int N, int K, const float *A, int lda, const float *B,
                                 int ldb, const float *C, int ldc) {
-    if (validate(M, N, K, A, lda, B, ldb, C, ldc) != hipSuccess) return -1;
-    return choose(M, N, K);
+    if (validate(SGEMM_F32_OP_N, SGEMM_F32_OP_N, M, N, K, 1.0f, A, lda, B, ldb, C, ldc) !=
+        hipSuccess)
+        return -1;
+    return choose(SGEMM_F32_OP_N, SGEMM_F32_OP_N, M, N, K);
 }
 
-extern "C" hipError_t sgemm_f32_algo(int M, int N, int K, const float *A, int lda,
-                                     const float *B, int ldb, float *C, int ldc,
-                                     hipStream_t stream, int algo) {
+extern "C" hipError_t sgemm_f32_ex_algo(int transa, int transb, int M, int N, int K, float alpha,
+                                        const float *A, int lda, const float *B, int ldb,
+                                        float beta, float *C, int ldc, hipStream_t stream,
+                                        int algo) {
     if (algo < 0 || algo >= SGEMM_F32_ALGO_COUNT) return hipErrorInvalidValue;
-    const hipError_t v = validate(M, N, K, A, lda, B, ldb, C, ldc);
-    if (v != hipSuccess) return v;
-    if (M == 0 || N == 0) return hipSuccess;
-    const Problem p{M, N, K, A, lda, B, ldb, C, ldc};
-    if (K == 0) return sgemm::launch_zero_fill(p, stream);
-    if (algo == SGEMM_F32_ALGO_AUTO) algo = choose(M, N, K);
+    if ((transa == SGEMM_F32_OP_T || transb == SGEMM_F32_OP_T) && !handles_transposes(algo))
+        return hipErrorInvalidValue;
+    hipError_t st;
+    if (trivial(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, &st))
+        return st;
+    const Problem p = problem(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    if (algo == SGEMM_F32_ALGO_AUTO) algo = choose(transa, transb, M, N, K);
     switch (algo) {
     case SGEMM_F32_ALGO_NAIVE: return sgemm::launch_naive(p, stream);
     case SGEMM_F32_ALGO_LDS_TILED: return sgemm::launch_lds_tiled(p, stream);
@@ -87,9 +133,32 @@ extern "C" hipError_t sgemm_f32_algo(int M, int N, int K, const float *A, int ld
     }
 }
 
+extern "C" hipError_t sgemm_f32_ex(int transa, int transb, int M, int N, int K, float alpha,
+                                   const float *A, int lda, const float *B, int ldb, float beta,
+                                   float *C, int ldc, hipStream_t stream) {
+    return sgemm_f32_ex_algo(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                             SGEMM_F32_ALGO_AUTO);
+}
+
+extern "C" hipError_t sgemm_f32_algo(int M, int N, int K, const float *A, int lda,
+                                     const float *B, int ldb, float *C, int ldc,
+                                     hipStream_t stream, int algo) {
+    return sgemm_f32_ex_algo(SGEMM_F32_OP_N, SGEMM_F32_OP_N, M, N, K, 1.0f, A, lda, B, ldb, 0.0f,
+                             C, ldc, stream, algo);
+}
+
 extern "C" hipError_t sgemm_f32(int M, int N, int K, const float *A, int lda, const float *B,
                                 int ldb, float *C, int ldc, hipStream_t stream) {
     return sgemm_f32_algo(M, N, K, A, lda, B, ldb, C, ldc, stream, SGEMM_F32_ALGO_AUTO);
+}
+
+extern "C" hipError_t sgemm_f32_colmajor(int transa, int transb, int M, int N, int K,
+                                         float alpha, const float *A, int lda, const float *B,
+                                         int ldb, float beta, float *C, int ldc,
+                                         hipStream_t stream) {
+    // A column-major array is the row-major array of its transpose, so
+    // C^T = alpha*op(B)^T*op(A)^T + beta*C^T in row-major terms.
+    return sgemm_f32_ex(transb, transa, N, M, K, alpha, B, ldb, A, lda, beta, C, ldc, stream);
 }
 
 extern "C" int sgemm_f32_mfma_tiles(void) { return sgemm::mfma_tile_count(); }
@@ -101,14 +170,21 @@ extern "C" int sgemm_f32_mfma_select(int M, int N, int K, int compute_units) {
     return sgemm::mfma_select(M, N, K, compute_units);
 }
 
+extern "C" hipError_t sgemm_f32_ex_mfma_tile(int transa, int transb, int M, int N, int K,
+                                             float alpha, const float *A, int lda,
+                                             const float *B, int ldb, float beta, float *C,
+                                             int ldc, hipStream_t stream, int tile) {
+    if (tile < 0 || tile >= sgemm::mfma_tile_count()) return hipErrorInvalidValue;
+    hipError_t st;
+    if (trivial(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, &st))
+        return st;
+    return sgemm::launch_mfma_tile(
+        problem(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), stream, tile);
+}
+
 extern "C" hipError_t sgemm_f32_mfma_tile(int M, int N, int K, const float *A, int lda,
                                           const float *B, int ldb, float *C, int ldc,
                                           hipStream_t stream, int tile) {
-    if (tile < 0 || tile >= sgemm::mfma_tile_count()) return hipErrorInvalidValue;
-    const hipError_t v = validate(M, N, K, A, lda, B, ldb, C, ldc);
-    if (v != hipSuccess) return v;
-    if (M == 0 || N == 0) return hipSuccess;
-    const Problem p{M, N, K, A, lda, B, ldb, C, ldc};
-    if (K == 0) return sgemm::launch_zero_fill(p, stream);
-    return sgemm::launch_mfma_tile(p, stream, tile);
+    return sgemm_f32_ex_mfma_tile(SGEMM_F32_OP_N, SGEMM_F32_OP_N, M, N, K, 1.0f, A, lda, B, ldb,
+                                  0.0f, C, ldc, stream, tile);
 }

@@ -30,7 +30,7 @@ __device__ __forceinline__ f32x4 load16_skinny(const float *p) {
 template <int MR, int LPR, int THREADS>
 __global__ __launch_bounds__(THREADS) void skinny_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
-    int64_t ldb, float *__restrict__ C, int64_t ldc) {
+    int64_t ldb, float *__restrict__ C, int64_t ldc, float alpha, float beta) {
     constexpr int CW = 4 * LPR;        // columns per work-group
     constexpr int S = THREADS / LPR;   // k slots (a power of two)
     constexpr int OUT = MR * CW;       // outputs per work-group
@@ -128,7 +128,10 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
     }
     for (int o = tid; o < OUT; o += THREADS) {
         const int m = o / CW, c = o % CW;
-        if (m < M && n0 + c < N) C[(int64_t)m * ldc + n0 + c] = red[0][o];
+        if (m < M && n0 + c < N) {
+            float *dst = C + (int64_t)m * ldc + n0 + c;
+            *dst = epilogue(red[0][o], alpha, beta, dst);
+        }
     }
 }
 
@@ -139,11 +142,11 @@ static hipError_t launch_rows(const Problem &p, hipStream_t s) {
     if (p.N >= 64 * 256) {
         const int64_t groups = (p.N + 63) / 64;
         return launch(skinny_kernel<MR, 16, THREADS>, dim3((unsigned)groups), dim3(THREADS), 0, s,
-                      p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
+                      p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta);
     }
     const int64_t groups = (p.N + 15) / 16;
     return launch(skinny_kernel<MR, 4, THREADS>, dim3((unsigned)groups), dim3(THREADS), 0, s, p.M,
-                  p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
+                  p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta);
 }
 
 hipError_t launch_skinny(const Problem &p, hipStream_t s) {

@@ -28,7 +28,8 @@ template <int NR, int RW>
 __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                                                        const float *__restrict__ A, int64_t lda,
                                                        const float *__restrict__ B, int64_t ldb,
-                                                       float *__restrict__ C, int64_t ldc) {
+                                                       float *__restrict__ C, int64_t ldc,
+                                                       float alpha, float beta) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * 4 + wave) * RW;
 
@@ -107,7 +108,10 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
             if (row0 + r < M)
 #pragma unroll
                 for (int j = 0; j < NR; ++j)
-                    if (j < N) C[(int64_t)(row0 + r) * ldc + j] = acc[r][j];
+                    if (j < N) {
+                        float *dst = C + (int64_t)(row0 + r) * ldc + j;
+                        *dst = epilogue(acc[r][j], alpha, beta, dst);
+                    }
     }
 }
 
@@ -118,7 +122,7 @@ static hipError_t launch_cols(const Problem &p, hipStream_t s) {
     const int64_t groups = (p.M + 4 * RW - 1) / (4 * RW);
     if (groups > INT32_MAX) return hipErrorInvalidValue;
     return launch(skinny_n_kernel<NR, RW>, dim3((unsigned)groups), dim3(256), 0, s, p.M, p.N, p.K,
-                  p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
+                  p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta);
 }
 
 hipError_t launch_skinny_n(const Problem &p, hipStream_t s) {

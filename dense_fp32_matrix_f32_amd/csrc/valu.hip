@@ -32,7 +32,8 @@ __global__ __launch_bounds__(VT) void valu_kernel(int M, int N, int K,
                                                   const float *__restrict__ A, int64_t lda,
                                                   const float *__restrict__ B, int64_t ldb,
                                                   float *__restrict__ C, int64_t ldc,
-                                                  int tiles_m, int tiles_n) {
+                                                  float alpha, float beta, int tiles_m,
+                                                  int tiles_n) {
     __shared__ __attribute__((aligned(16))) float As[2][VK][VPITCH];
     __shared__ __attribute__((aligned(16))) float Bs[2][VK][VPITCH];
 
@@ -129,11 +130,11 @@ __global__ __launch_bounds__(VT) void valu_kernel(int M, int N, int K,
             float *dst = C + (int64_t)row * ldc + col;
             if (full) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[e] = acc[i][h * 4 + e];
+                for (int e = 0; e < 4; ++e) dst[e] = epilogue(acc[i][h * 4 + e], alpha, beta, dst + e);
             } else if (row < M) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (col + e < N) dst[e] = acc[i][h * 4 + e];
+                    if (col + e < N) dst[e] = epilogue(acc[i][h * 4 + e], alpha, beta, dst + e);
             }
         }
     }
@@ -143,7 +144,8 @@ hipError_t launch_valu_regblock(const Problem &p, hipStream_t s) {
     const int64_t tiles_m = (p.M + VB - 1) / VB, tiles_n = (p.N + VB - 1) / VB;
     if (tiles_m * tiles_n > INT32_MAX) return hipErrorInvalidValue;
     return launch(valu_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(VT), 0, s, p.M, p.N, p.K,
-                  p.A, p.lda, p.B, p.ldb, p.C, p.ldc, (int)tiles_m, (int)tiles_n);
+                  p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta, (int)tiles_m,
+                  (int)tiles_n);
 }
 
 }  // namespace sgemm

@@ -101,6 +101,58 @@ int sgemm_f32_select(int M, int N, int K,
 const char *sgemm_f32_algo_name(int algo);
 
 /*
+ * General form, as in the BLAS interface of the library the pages measure
+ * themselves against (cuBLAS, page "CUDA算子优化(4)：矩阵乘法"):
+ *     C = alpha * op(A) * op(B) + beta * C
+ * with op(A) M x K and op(B) K x N, all arrays row-major:
+ *   transa = SGEMM_F32_OP_N: A is the M x K array A[i*lda + k], lda >= max(1,K);
+ *   transa = SGEMM_F32_OP_T: A is a K x M array and op(A)[i][k] = A[k*lda + i],
+ *                            lda >= max(1,M);
+ *   transb = SGEMM_F32_OP_N: B is the K x N array B[k*ldb + j], ldb >= max(1,N);
+ *   transb = SGEMM_F32_OP_T: B is an N x K array and op(B)[k][j] = B[j*ldb + k],
+ *                            ldb >= max(1,K);
+ *   C is M x N, C[i*ldc + j], ldc >= max(1,N), read and written.
+ * beta == 0 means C is not read (NaN or Inf there does not reach the result);
+ * alpha == 0 or K == 0 means A and B are not read and C becomes beta*C.  The
+ * scaling is alpha*sum + beta*C in fp32 after the sum, fused where possible.
+ * Ownership, asynchrony, reproducibility and errors are as for sgemm_f32();
+ * a transa or transb other than the two values below is hipErrorInvalidValue,
+ * and A and B may be NULL when alpha == 0 or K == 0.  sgemm_f32() is
+ * sgemm_f32_ex(N, N, M, N, K, 1, A, lda, B, ldb, 0, C, ldc), bit for bit.
+ *
+ * sgemm_f32_ex_algo() forces one rung.  AUTO, NAIVE, LDS_TILED and MFMA accept
+ * either storage order; VALU_REGBLOCK, SKINNY and SKINNY_N accept only
+ * SGEMM_F32_OP_N for both operands (hipErrorInvalidValue otherwise).  AUTO
+ * uses the SKINNY and SKINNY_N rules of sgemm_f32() for untransposed operands
+ * and MFMA for every other product.
+ *
+ * sgemm_f32_colmajor() takes the same arguments with every array column-major,
+ * as in the reference BLAS sgemm: A is M x K (transa = N, lda >= max(1,M)) or
+ * K x M (transa = T, lda >= max(1,K)), B is K x N (ldb >= max(1,K)) or N x K
+ * (ldb >= max(1,N)), C is M x N with ldc >= max(1,M).  A column-major array is
+ * the row-major array of its transpose, so this is the row-major product
+ * C^T = alpha * op(B)^T * op(A)^T + beta * C^T, computed by sgemm_f32_ex().
+ */
+#define SGEMM_F32_OP_N 0 /* operand as stored */
+#define SGEMM_F32_OP_T 1 /* operand transposed */
+
+hipError_t sgemm_f32_ex(int transa, int transb, int M, int N, int K, float alpha,
+                        const float *A, int lda,
+                        const float *B, int ldb, float beta,
+                        float *C, int ldc,
+                        hipStream_t stream);
+hipError_t sgemm_f32_ex_algo(int transa, int transb, int M, int N, int K, float alpha,
+                             const float *A, int lda,
+                             const float *B, int ldb, float beta,
+                             float *C, int ldc,
+                             hipStream_t stream, int algo);
+hipError_t sgemm_f32_colmajor(int transa, int transb, int M, int N, int K, float alpha,
+                              const float *A, int lda,
+                              const float *B, int ldb, float beta,
+                              float *C, int ldc,
+                              hipStream_t stream);
+
+/*
  * Tile configurations of the matrix-core rung (SGEMM_F32_ALGO_MFMA), for
  * tuning and tests.  The rung tiles C into BM x BN blocks, one work-group per
  * block, as in the shared-memory tiling of the page "CUDA算子优化(4)：矩阵乘法"
@@ -120,6 +172,7 @@ const char *sgemm_f32_algo_name(int algo);
  * sgemm_f32_mfma_tile()       same operation and contract as sgemm_f32(), on the
  *                             matrix-core rung with configuration `tile`; an
  *                             unknown id is hipErrorInvalidValue.
+ * sgemm_f32_ex_mfma_tile()    the same for the general form of sgemm_f32_ex().
  */
 int sgemm_f32_mfma_tiles(void);
 const char *sgemm_f32_mfma_tile_name(int tile);
@@ -129,6 +182,11 @@ hipError_t sgemm_f32_mfma_tile(int M, int N, int K,
                                const float *B, int ldb,
                                float *C, int ldc,
                                hipStream_t stream, int tile);
+hipError_t sgemm_f32_ex_mfma_tile(int transa, int transb, int M, int N, int K, float alpha,
+                                  const float *A, int lda,
+                                  const float *B, int ldb, float beta,
+                                  float *C, int ldc,
+                                  hipStream_t stream, int tile);
 
 #ifdef __cplusplus
 }

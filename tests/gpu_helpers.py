@@ -43,7 +43,7 @@ class Device:
     logical matrix; columns N..ldc-1 of every row also hold the sentinel.
     """
 
-    def __init__(self, A, B, M, N, K, ldc=None, offset_elems=0, fill=SENTINEL):
+    def __init__(self, A, B, M, N, K, ldc=None, offset_elems=0, fill=SENTINEL, c_init=None):
         torch = torch_cuda()
         self.torch = torch
         self.M, self.N, self.K = M, N, K
@@ -59,6 +59,10 @@ class Device:
         self.b_ptr = self.b_buf.data_ptr() + 4 * o
         self.c_ptr = self.c_buf.data_ptr() + 4 * (o + self.ldc)
         self.offset = o
+        if c_init is not None:
+            # the logical C (rows 1..M of the buffer, columns 0..N-1) starts as c_init
+            view = self.c_buf[o + self.ldc:o + self.ldc + M * self.ldc].view(M, self.ldc)
+            view[:, :N] = torch.from_numpy(np.ascontiguousarray(c_init, dtype=np.float32)).cuda()
 
     def run(self, algo=sg.ALGO_AUTO, stream=None):
         torch = self.torch
@@ -77,6 +81,21 @@ class Device:
                                     self.ldb, self.c_ptr, self.ldc, s.cuda_stream, tile)
         if st != 0:
             raise sg.SgemmError(st, "sgemm_f32_mfma_tile")
+        s.synchronize()
+
+    def run_ex(self, transa, transb, alpha, beta, algo=sg.ALGO_AUTO, tile=None, stream=None):
+        """C = alpha*op(A)*op(B) + beta*C through sgemm_f32_ex_algo, or the matrix-core
+        rung with configuration `tile`."""
+        torch = self.torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        args = (transa, transb, self.M, self.N, self.K, alpha, self.a_ptr, self.lda, self.b_ptr,
+                self.ldb, beta, self.c_ptr, self.ldc, s.cuda_stream)
+        if tile is None:
+            st = sg.sgemm_f32_ex_algo(*args, algo)
+        else:
+            st = sg.sgemm_f32_ex_mfma_tile(*args, tile)
+        if st != 0:
+            raise sg.SgemmError(st, "sgemm_f32_ex")
         s.synchronize()
 
     def result(self):
@@ -126,5 +145,30 @@ def check_sampled(A, B, M, N, K, Cg, what, exact=False, seed=0):
     g = Cg[r, c]
     if exact:
         assert np.array_equal(g.astype(np.float64), Cref), f"{what}: sampled not bitwise exact"
+        return 0.0
+    return assert_close(g, Cref, S, what)
+
+
+def stored(X, trans, ld=None):
+    """The row-major array that holds X (rows x cols) as an operand passed with
+    `trans`: X itself, or its transpose; padding columns hold NaN."""
+    Y = np.ascontiguousarray(X.T) if trans else np.ascontiguousarray(X)
+    if ld is None or ld == Y.shape[1]:
+        return Y
+    out = np.full((Y.shape[0], ld), np.nan, dtype=np.float32)
+    out[:, :Y.shape[1]] = Y
+    return out
+
+
+def check_ex(As, Bs, M, N, K, ta, tb, alpha, beta, C0, Cg, what, exact=False, rows=None,
+             cols=None):
+    """Compare the GPU result of the general form with the oracle (whole, or the
+    listed elements).  As and Bs are the stored arrays, possibly padded."""
+    Av = As[:, :(M if ta else K)]
+    Bv = Bs[:, :(K if tb else N)]
+    Cref, S = oracle.sgemm_ex(Av, Bv, ta, tb, alpha, beta, C0, rows=rows, cols=cols)
+    g = Cg if rows is None else Cg[rows, cols]
+    if exact:
+        assert np.array_equal(g.astype(np.float64), Cref), f"{what}: not bitwise exact"
         return 0.0
     return assert_close(g, Cref, S, what)

@@ -186,3 +186,53 @@ def test_mfma_tile_choice_against_measured_timings():
         assert by_name[chosen] <= 1.05 * best, (shape, chosen, by_name)
         exact += by_name[chosen] == best
     assert exact >= 12
+
+
+# ---- general form ----
+def _ex(**kw):
+    base = dict(ta=0, tb=0, M=8, N=16, K=8, alpha=1.0, A=A_ADDR, lda=8, B=B_ADDR, ldb=16,
+                beta=0.0, C=C_ADDR, ldc=16)
+    base.update(kw)
+    return sg.sgemm_f32_ex_algo(base["ta"], base["tb"], base["M"], base["N"], base["K"],
+                                base["alpha"], base["A"], base["lda"], base["B"], base["ldb"],
+                                base["beta"], base["C"], base["ldc"], 0, base.get("algo", 0))
+
+
+@pytest.mark.parametrize("args", [
+    dict(ta=2), dict(tb=-1),                          # unknown storage orders
+    dict(ta=1, lda=7),                                # transposed A: lda >= M (8)
+    dict(tb=1, ldb=7),                                # transposed B: ldb >= K (8)
+    dict(ta=1, K=20, lda=8, C=A_ADDR + 4 * 100),      # C inside the K x M extent of A^T
+    dict(C=0), dict(A=0), dict(B=0), dict(ldc=15),
+])
+def test_ex_invalid_arguments(args):
+    assert _ex(**args) == INVALID, args
+
+
+def test_ex_transposed_ld_rules_accept():
+    # with transposes, lda >= M and ldb >= K are enough (no device: the launch fails
+    # with a device error, not with an argument error)
+    st = _ex(ta=1, tb=1, M=8, N=16, K=4, lda=8, ldb=4)
+    assert st != INVALID
+
+
+def test_ex_untransposed_only_rungs():
+    for algo in (sg.ALGO_VALU_REGBLOCK, sg.ALGO_SKINNY, sg.ALGO_SKINNY_N):
+        assert _ex(ta=1, lda=8, algo=algo) == INVALID
+        assert _ex(tb=1, ldb=8, algo=algo) == INVALID
+
+
+def test_ex_product_free_arguments():
+    # alpha == 0 or K == 0: A and B may be NULL (nothing is read from them)
+    assert _ex(alpha=0.0, A=0, B=0) != INVALID
+    assert _ex(K=0, A=0, B=0, lda=1) != INVALID
+    # empty C: nothing to do at all, success even without a device
+    assert _ex(M=0, C=0, A=0, B=0) == 0
+
+
+def test_colmajor_maps_to_row_major():
+    # column-major C is M x N with ldc >= M
+    st = sg.sgemm_f32_colmajor(0, 0, 16, 8, 8, 1.0, A_ADDR, 16, B_ADDR, 8, 0.0, C_ADDR, 15, 0)
+    assert st == INVALID
+    st = sg.sgemm_f32_colmajor(0, 0, 16, 8, 8, 1.0, A_ADDR, 16, B_ADDR, 8, 0.0, C_ADDR, 16, 0)
+    assert st != INVALID
