@@ -320,15 +320,18 @@ def tile_sweep(torch, sg, shapes, args):
     """Kernel time of every tile configuration of the matrix-core rung on each shape
     (one JSON line per shape and configuration)."""
     stream = torch.cuda.current_stream()
+    ta, tb = (int(args.layout[0] == "T"), int(args.layout[1] == "T"))
     for (M, N, K) in shapes:
-        _, _, dA, dB, dC = make_inputs(torch, M, N, K, args.seed)
+        _, _, dA, dB, dC = make_inputs(torch, M, N, K, args.seed, layout=(ta, tb))
         flops = algorithmic_flops(M, N, K)
+        lda, ldb = (M if ta else K), (K if tb else N)
 
         def launch(tile):
-            st = sg.sgemm_f32_mfma_tile(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N,
-                                        dC.data_ptr(), N, stream.cuda_stream, tile)
+            st = sg.sgemm_f32_ex_mfma_tile(ta, tb, M, N, K, 1.0, dA.data_ptr(), lda,
+                                           dB.data_ptr(), ldb, 0.0, dC.data_ptr(), N,
+                                           stream.cuda_stream, tile)
             if st != 0:
-                raise sg.SgemmError(st, "sgemm_f32_mfma_tile")
+                raise sg.SgemmError(st, "sgemm_f32_ex_mfma_tile")
 
         def timed(tile, n):
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -350,7 +353,7 @@ def tile_sweep(torch, sg, shapes, args):
             timed(tile, max(2, min(2000, int(50 / est))))
             kms = timed(tile, max(args.steps, min(2000, int(150 / est))))
             avg = sum(kms) / len(kms)
-            print(json.dumps({"shape": [M, N, K], "tile": tile,
+            print(json.dumps({"shape": [M, N, K], "layout": args.layout, "tile": tile,
                               "name": sg.sgemm_f32_mfma_tile_name(tile), "chosen": tile == auto,
                               "kernel_ms_avg": round(avg, 5), "kernel_ms_min": round(min(kms), 5),
                               "tflops": round(flops / (avg * 1e-3) / 1e12, 2), "steps": len(kms)}),
