@@ -7,7 +7,7 @@ memory and the stream, the library does all of the arithmetic.
 """
 from __future__ import annotations
 
-from ._binding import (ALGO_AUTO, ALGO_COUNT, ALGO_LDS_TILED, ALGO_MFMA, ALGO_NAIVE,
+from ._binding import (ALGO_AUTO, ALGO_BF16X6, ALGO_COUNT, ALGO_LDS_TILED, ALGO_MFMA, ALGO_NAIVE,
                        ALGO_SKINNY, ALGO_SKINNY_N, ALGO_VALU_REGBLOCK, ALGOS, EXPORTED, LIB_PATH,
                        OP_N, OP_T, SgemmError, lib, sgemm_f32, sgemm_f32_algo, sgemm_f32_algo_name,
                        sgemm_f32_colmajor, sgemm_f32_ex, sgemm_f32_ex_algo,

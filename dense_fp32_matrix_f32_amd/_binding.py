@@ -19,10 +19,11 @@ ALGO_VALU_REGBLOCK = 3
 ALGO_MFMA = 4
 ALGO_SKINNY = 5
 ALGO_SKINNY_N = 6
-ALGO_COUNT = 7
+ALGO_BF16X6 = 7
+ALGO_COUNT = 8
 ALGOS = {"auto": ALGO_AUTO, "naive": ALGO_NAIVE, "lds_tiled": ALGO_LDS_TILED,
          "valu_regblock": ALGO_VALU_REGBLOCK, "mfma": ALGO_MFMA, "skinny": ALGO_SKINNY,
-         "skinny_n": ALGO_SKINNY_N}
+         "skinny_n": ALGO_SKINNY_N, "bf16x6": ALGO_BF16X6}
 
 HIP_SUCCESS = 0
 HIP_ERROR_INVALID_VALUE = 1

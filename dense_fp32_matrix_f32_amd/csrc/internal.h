@@ -55,6 +55,9 @@ int mfma_tile_count();
 const char *mfma_tile_name(int tile);
 // The configuration launch_mfma() uses for this shape on `cus` compute units.
 int mfma_select(int M, int N, int K, int cus);
+// The fp32 product on the bf16 matrix cores with three-part operand splitting
+// (untransposed operands only).
+hipError_t launch_split(const Problem &p, hipStream_t s);
 hipError_t launch_skinny(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_n(const Problem &p, hipStream_t s);
 

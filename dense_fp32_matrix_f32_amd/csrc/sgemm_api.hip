@@ -98,6 +98,7 @@ extern "C" const char *sgemm_f32_algo_name(int algo) {
     case SGEMM_F32_ALGO_MFMA: return "mfma";
     case SGEMM_F32_ALGO_SKINNY: return "skinny";
     case SGEMM_F32_ALGO_SKINNY_N: return "skinny_n";
+    case SGEMM_F32_ALGO_BF16X6: return "bf16x6";
     default: return "invalid";
     }
 }
@@ -129,6 +130,7 @@ extern "C" hipError_t sgemm_f32_ex_algo(int transa, int transb, int M, int N, in
     case SGEMM_F32_ALGO_MFMA: return sgemm::launch_mfma(p, stream);
     case SGEMM_F32_ALGO_SKINNY: return sgemm::launch_skinny(p, stream);
     case SGEMM_F32_ALGO_SKINNY_N: return sgemm::launch_skinny_n(p, stream);
+    case SGEMM_F32_ALGO_BF16X6: return sgemm::launch_split(p, stream);
     default: return hipErrorInvalidValue;
     }
 }

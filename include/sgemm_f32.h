@@ -58,7 +58,8 @@ extern "C" {
 #define SGEMM_F32_ALGO_MFMA 4          /* LDS double buffer, fp32 matrix cores */
 #define SGEMM_F32_ALGO_SKINNY 5        /* M <= 8: stream B once, split K in the work-group */
 #define SGEMM_F32_ALGO_SKINNY_N 6      /* N <= 8: stream A once, split K across a wave */
-#define SGEMM_F32_ALGO_COUNT 7
+#define SGEMM_F32_ALGO_BF16X6 7        /* bf16 matrix cores, operands split in 3 parts (below) */
+#define SGEMM_F32_ALGO_COUNT 8
 
 /*
  * C = A·B with the algorithm chosen for the shape (SGEMM_F32_ALGO_AUTO).
@@ -86,6 +87,20 @@ hipError_t sgemm_f32_algo(int M, int N, int K,
                           const float *B, int ldb,
                           float *C, int ldc,
                           hipStream_t stream, int algo);
+
+/*
+ * SGEMM_F32_ALGO_BF16X6 is never chosen automatically.  It computes the same
+ * fp32 product on the bf16 matrix cores, the reduced-precision matrix step the
+ * pages end with (their "Tensor Core" outlook): every value of A and B is split
+ * exactly into three bf16 parts, x = x0 + x1 + x2, and the six part products
+ * with p + q <= 2 are accumulated in fp32, smallest first.  The dropped terms
+ * are below 2^-24 of each product, so the result has fp32 accuracy (within the
+ * same bound as the other algorithms; all-ones, identity and small-integer
+ * products are exact).  Differences from the fp32 rungs: an infinite input
+ * gives NaN instead of +-Inf in its row or column (Inf times a zero part), and
+ * values above about 3.39e38 in magnitude, whose bf16 rounding overflows,
+ * become infinite.  Untransposed operands only.
+ */
 
 /*
  * The algorithm SGEMM_F32_ALGO_AUTO picks for these arguments (host-only:

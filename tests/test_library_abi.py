@@ -217,7 +217,7 @@ def test_ex_transposed_ld_rules_accept():
 
 
 def test_ex_untransposed_only_rungs():
-    for algo in (sg.ALGO_VALU_REGBLOCK, sg.ALGO_SKINNY, sg.ALGO_SKINNY_N):
+    for algo in (sg.ALGO_VALU_REGBLOCK, sg.ALGO_SKINNY, sg.ALGO_SKINNY_N, sg.ALGO_BF16X6):
         assert _ex(ta=1, lda=8, algo=algo) == INVALID
         assert _ex(tb=1, ldb=8, algo=algo) == INVALID
 

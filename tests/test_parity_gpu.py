@@ -21,8 +21,8 @@ from gpu_helpers import (Device, assert_close, assert_guards, check_full, check_
 
 pytestmark = pytest.mark.gpu
 
-LADDER = [sg.ALGO_NAIVE, sg.ALGO_LDS_TILED, sg.ALGO_VALU_REGBLOCK, sg.ALGO_MFMA, sg.ALGO_SKINNY,
-          sg.ALGO_SKINNY_N, sg.ALGO_AUTO]
+LADDER = [sg.ALGO_NAIVE, sg.ALGO_LDS_TILED, sg.ALGO_VALU_REGBLOCK, sg.ALGO_MFMA, sg.ALGO_BF16X6,
+          sg.ALGO_SKINNY, sg.ALGO_SKINNY_N, sg.ALGO_AUTO]
 FAST = [sg.ALGO_VALU_REGBLOCK, sg.ALGO_MFMA, sg.ALGO_AUTO]
 name = sg.sgemm_f32_algo_name
 
@@ -117,7 +117,7 @@ def test_2048x3072x4096(algo):
 
 
 # ---------------------------------------------------------------- ragged 4095 x 4097 x 1023
-@pytest.mark.parametrize("algo", LADDER[:4] + [sg.ALGO_AUTO], ids=name)
+@pytest.mark.parametrize("algo", LADDER[:5] + [sg.ALGO_AUTO], ids=name)
 def test_ragged_4095x4097x1023(algo):
     M, N, K = 4095, 4097, 1023
     A, B = inputs(M, N, K, "uniform_pm1", seed=4)
@@ -141,7 +141,7 @@ def test_row_times_matrix_1x4096x4096(algo):
 
 
 # ---------------------------------------------------------------- 8192^3
-@pytest.mark.parametrize("algo", [sg.ALGO_AUTO, sg.ALGO_VALU_REGBLOCK], ids=name)
+@pytest.mark.parametrize("algo", [sg.ALGO_AUTO, sg.ALGO_VALU_REGBLOCK, sg.ALGO_BF16X6], ids=name)
 def test_8192_cubed(algo):
     n = 8192
     A, B = inputs(n, n, n, "normal", seed=6)
@@ -204,7 +204,8 @@ def test_nan_stays_in_its_row_and_column(algo):
     assert not np.any(np.isfinite(np.delete(C[:, 101], 17)))
 
 
-@pytest.mark.parametrize("algo", FAST + [sg.ALGO_SKINNY, sg.ALGO_SKINNY_N], ids=name)
+@pytest.mark.parametrize("algo", FAST + [sg.ALGO_SKINNY, sg.ALGO_SKINNY_N, sg.ALGO_BF16X6],
+                         ids=name)
 def test_bitwise_reproducible(algo):
     M, N, K = 1000, 1100, 700
     A, B = inputs(M, N, K, "normal", seed=11)
