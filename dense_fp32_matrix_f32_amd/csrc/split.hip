@@ -18,17 +18,19 @@
 // above about 3.39e38) become infinite, and an infinite input makes its row or
 // column of C NaN rather than +-Inf (its residual parts are not numbers).
 //
-// Layout of the work is that of the fp32 rung (mfma_kernel.h): a 256 x 128 block
-// of C per work-group, four waves of 128 x 64, k windows of 16 in a three-stage
-// LDS ring with one barrier per window and the next window's fragments read
-// during the current one's MFMAs.  Global loads run two windows ahead into
-// registers; the split into parts happens when a window goes from registers to
-// LDS, so each value is split once per work-group.  Both operands are kept in
+// Layout of the work follows the fp32 rung (mfma_kernel.h): a block of C per
+// work-group (256 x 256 or 256 x 128), eight waves (two per SIMD, so that one
+// wave's part splitting and LDS waits overlap the other's MFMAs), k windows of
+// 16 in a three-stage LDS ring with one barrier per window.  Global loads run
+// ahead into registers; the split into parts happens when a window goes from
+// registers to LDS, so each value is split once per work-group.  Both operands are kept in
 // LDS with k contiguous (B is gathered column by column from global memory), as
 // rows of 16 bf16 per part whose two 16-byte halves swap places on every other
 // group of 8 rows, which keeps the fragment reads free of bank conflicts.
 // v_mfma_f32_32x32x16_bf16: lane l supplies row (column) l % 32 and eight
 // consecutive k starting at 8*(l / 32), the same k for A and B.
+#include <cmath>
+
 #include "mfma_kernel.h"
 
 namespace sgemm {
@@ -38,25 +40,53 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 namespace split {
 
-constexpr int BM = 256, BN = 128, BK = 16;
-constexpr int WM = 128, WN = 64, TM = WM / 32, TN = WN / 32;
-constexpr int WAVES_N = BN / WN;
-constexpr int THREADS = (BM / WM) * WAVES_N * 64;
-constexpr int STAGES = 3;
+constexpr int BK = 16;
 constexpr int PARTS = 3;
-constexpr int GROUP_M = 8;
-// bf16 elements of one part of one operand window, and of one LDS stage
-constexpr int A_PART = BM * BK, B_PART = BN * BK;
-constexpr int STAGE = PARTS * (A_PART + B_PART);
-// global -> register work per thread and window: A as runs of 8 k of one row,
-// B as runs of 8 k of one column
-constexpr int A_RUNS = BM * BK / 8 / THREADS;
-constexpr int B_RUNS = BN * BK / 8 / THREADS;
-static_assert(A_RUNS * THREADS * 8 == BM * BK && B_RUNS * THREADS * 8 == BN * BK, "whole runs");
-static_assert(STAGES * STAGE * 2 <= 160 * 1024, "LDS budget");
 
-// Element offset (bf16 units) of the 8-wide k half `h` of row `row` in a part.
-__device__ __forceinline__ int slot(int row, int h) { return row * BK + 8 * (h ^ ((row >> 3) & 1)); }
+// BM x BN block of C per work-group, WM x WN per wave, STAGES LDS buffers, OCC
+// work-groups per CU that the register allocation must allow.
+// FRAGS: 2 reads the next window's fragments during the current one's MFMAs
+// (one wave per SIMD); 1 reads each window's fragments at its start and leaves
+// the wait to be covered by the other waves of the SIMD (fewer registers); 0
+// does the same for A and reads the parts of B one at a time between the MFMAs
+// that use them (fewer registers still).
+// SLOTS: windows held in registers between their global loads and their LDS
+// stores (the loads run 2 + SLOTS windows ahead of the MFMAs).
+// RUN: consecutive k (4 or 8) of one row of A or column of B that a work-item
+// loads, splits and stores as one piece.
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_ = 3, int OCC_ = 1, int GROUP_M_ = 8,
+          int FRAGS_ = 2, int SLOTS_ = 2, int RUN_ = 8>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    static constexpr int OCC = OCC_, GROUP_M = GROUP_M_, FRAGS = FRAGS_, SLOTS = SLOTS_;
+    static constexpr int RUN = RUN_;
+    static_assert(FRAGS >= 0 && FRAGS <= 2, "fragment buffers");
+    static_assert(SLOTS == 1 || SLOTS == 2, "register slots");
+    static_assert(RUN == 4 || RUN == 8, "runs of 4 or 8 k");
+    static constexpr int TM = WM / 32, TN = WN / 32;
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int THREADS = (BM / WM) * WAVES_N * 64;
+    // bf16 elements of one part of one operand window, and of one LDS stage
+    static constexpr int A_PART = BM * BK, B_PART = BN * BK;
+    static constexpr int STAGE = PARTS * (A_PART + B_PART);
+    // global -> register work per thread and window: A as runs of RUN k of one
+    // row, B as runs of RUN k of one column
+    static constexpr int A_RUNS = BM * BK / RUN / THREADS;
+    static constexpr int B_RUNS = BN * BK / RUN / THREADS;
+    static constexpr int RPR = BK / RUN;  // runs per row (column)
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tiling");
+    static_assert(A_RUNS >= 1 && B_RUNS >= 1 && A_RUNS * THREADS * RUN == BM * BK &&
+                      B_RUNS * THREADS * RUN == BN * BK,
+                  "whole runs");
+    static_assert(STAGES == 3, "three-stage ring");
+    static_assert(STAGES * STAGE * 2 <= 160 * 1024, "LDS budget");
+};
+
+// Element offset (bf16 units) of element k of row `row` in a part: the two
+// 8-wide halves of a row swap places on every other group of 8 rows.
+__device__ __forceinline__ int slot(int row, int k) {
+    return row * BK + 8 * ((k >> 3) ^ ((row >> 3) & 1)) + (k & 7);
+}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -69,10 +99,24 @@ __device__ __forceinline__ unsigned to_bf16x2(float x, float y) {
 // The three bf16 parts of eight floats (see the file comment), two at a time:
 // the value of a part is read back from its bits, so each pair needs one
 // conversion per part.  An infinite input leaves NaN residuals.
-__device__ __forceinline__ void split3(const f32x8 &x, bf16x8 &p0, bf16x8 &p1, bf16x8 &p2) {
-    u32x4 w0, w1, w2;
+template <int R> struct Run;
+template <> struct Run<8> {
+    typedef f32x8 f;
+    typedef bf16x8 b;
+    typedef u32x4 u;
+};
+template <> struct Run<4> {
+    typedef f32x4 f;
+    typedef __bf16 b __attribute__((ext_vector_type(4)));
+    typedef unsigned u __attribute__((ext_vector_type(2)));
+};
+
+template <int R>
+__device__ __forceinline__ void split3(const typename Run<R>::f &x, typename Run<R>::b &p0,
+                                       typename Run<R>::b &p1, typename Run<R>::b &p2) {
+    typename Run<R>::u w0, w1, w2;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < R / 2; ++e) {
         const float a = x[2 * e], b = x[2 * e + 1];
         const unsigned u0 = to_bf16x2(a, b);
         const float ra = a - __builtin_bit_cast(float, u0 << 16);
@@ -84,9 +128,32 @@ __device__ __forceinline__ void split3(const f32x8 &x, bf16x8 &p0, bf16x8 &p1, b
         w1[e] = u1;
         w2[e] = to_bf16x2(sa, sb);
     }
-    p0 = __builtin_bit_cast(bf16x8, w0);
-    p1 = __builtin_bit_cast(bf16x8, w1);
-    p2 = __builtin_bit_cast(bf16x8, w2);
+    p0 = __builtin_bit_cast(typename Run<R>::b, w0);
+    p1 = __builtin_bit_cast(typename Run<R>::b, w1);
+    p2 = __builtin_bit_cast(typename Run<R>::b, w2);
+}
+
+// Scheduling hint for the steady-state body: each of its MF MFMAs is followed by
+// at most one memory instruction (the DSR LDS reads, then the DSW LDS writes,
+// then the VMR global loads) and up to VPS vector-ALU instructions (the splits),
+// so the matrix cores keep running while the parts are computed.  Bodies with
+// fewer MFMAs than memory instructions are left to the default scheduler.
+template <int MF, int DSR, int DSW, int VMR, int VPS>
+__device__ __forceinline__ void interleave_split() {
+    if constexpr (MF >= DSR + DSW + VMR) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (i < DSR) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        } else if (i < DSR + DSW) {
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        } else if (i < DSR + DSW + VMR) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, VPS, 0);    // vector ALU
+    }
+    }
 }
 
 // The six part products (p, q), smallest first.
@@ -103,38 +170,47 @@ struct Args {
     float alpha, beta;
 };
 
-__global__ __launch_bounds__(THREADS, 1) void split_kernel(Args g, int tiles_m, int tiles_n) {
+template <class T>
+__global__ __launch_bounds__(T::THREADS, T::OCC) void split_kernel(Args g, int tiles_m,
+                                                                  int tiles_n) {
+    constexpr int BM = T::BM, BN = T::BN, WM = T::WM, WN = T::WN, TM = T::TM, TN = T::TN;
+    constexpr int THREADS = T::THREADS, WAVES_N = T::WAVES_N, STAGES = T::STAGES;
+    constexpr int A_PART = T::A_PART, B_PART = T::B_PART, STAGE = T::STAGE;
+    constexpr int A_RUNS = T::A_RUNS, B_RUNS = T::B_RUNS;
     __shared__ __attribute__((aligned(16))) __bf16 lds[STAGES * STAGE];
     const int M = g.M, N = g.N, K = g.K;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, lh = lane >> 5;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     int tm, tn;
-    tile_order(blockIdx.x, tiles_m, tiles_n, GROUP_M, &tm, &tn);
+    tile_order(blockIdx.x, tiles_m, tiles_n, T::GROUP_M, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     // ---- global -> register assignment ----
+    constexpr int RUN = T::RUN, RPR = T::RPR;
+    typedef typename Run<RUN>::f fR;
+    typedef typename Run<RUN>::b bR;
     const float *a_src[A_RUNS];
-    int a_row[A_RUNS], a_h[A_RUNS];
+    int a_row[A_RUNS], a_k[A_RUNS];
 #pragma unroll
     for (int v = 0; v < A_RUNS; ++v) {
-        const int c = tid + v * THREADS;  // run c: row c / 2, k half c % 2
-        a_row[v] = c >> 1;
-        a_h[v] = c & 1;
-        a_src[v] = g.A + (int64_t)min(m0 + a_row[v], M - 1) * g.lda + 8 * a_h[v];
+        const int c = tid + v * THREADS;  // run c: row c / RPR, k RUN * (c % RPR)
+        a_row[v] = c / RPR;
+        a_k[v] = RUN * (c % RPR);
+        a_src[v] = g.A + (int64_t)min(m0 + a_row[v], M - 1) * g.lda + a_k[v];
     }
     const float *b_src[B_RUNS];
-    int b_col[B_RUNS], b_h[B_RUNS];
+    int b_col[B_RUNS], b_k[B_RUNS];
 #pragma unroll
     for (int v = 0; v < B_RUNS; ++v) {
-        const int c = tid + v * THREADS;  // run c: column c % BN, k half c / BN
+        const int c = tid + v * THREADS;  // run c: column c % BN, k RUN * (c / BN)
         b_col[v] = c % BN;
-        b_h[v] = c / BN;
-        b_src[v] = g.B + (int64_t)(8 * b_h[v]) * g.ldb + min(n0 + b_col[v], N - 1);
+        b_k[v] = RUN * (c / BN);
+        b_src[v] = g.B + (int64_t)b_k[v] * g.ldb + min(n0 + b_col[v], N - 1);
     }
 
-    // Two register slots of fetched windows.
-    f32x8 ra[2][A_RUNS], rb[2][B_RUNS];
+    // Register slots of fetched windows.
+    fR ra[T::SLOTS][A_RUNS], rb[T::SLOTS][B_RUNS];
 
     // Window w (k = 16w .. 16w+15) into slot s.  FULL: every k < K.
     auto fetch = [&](auto full_tag, int s, int w) {
@@ -144,20 +220,26 @@ __global__ __launch_bounds__(THREADS, 1) void split_kernel(Args g, int tiles_m, 
         for (int v = 0; v < A_RUNS; ++v) {
             const float *p = a_src[v] + k0;
             if constexpr (FULL) {
-                const f32x4 lo = load16(p), hi = load16(p + 4);
-                ra[s][v] = f32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            } else {
-                const int64_t kk = k0 + 8 * a_h[v];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ra[s][v][e] = kk + e < K ? p[e] : 0.0f;
+                for (int e4 = 0; e4 < RUN / 4; ++e4) {
+                    const f32x4 q = load16(p + 4 * e4);
+                    ra[s][v][4 * e4 + 0] = q.x;
+                    ra[s][v][4 * e4 + 1] = q.y;
+                    ra[s][v][4 * e4 + 2] = q.z;
+                    ra[s][v][4 * e4 + 3] = q.w;
+                }
+            } else {
+                const int64_t kk = k0 + a_k[v];
+#pragma unroll
+                for (int e = 0; e < RUN; ++e) ra[s][v][e] = kk + e < K ? p[e] : 0.0f;
             }
         }
 #pragma unroll
         for (int v = 0; v < B_RUNS; ++v) {
             const float *p = b_src[v] + k0 * g.ldb;
-            const int64_t kk = k0 + 8 * b_h[v];
+            const int64_t kk = k0 + b_k[v];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < RUN; ++e) {
                 if constexpr (FULL) {
                     rb[s][v][e] = p[(int64_t)e * g.ldb];
                 } else {
@@ -171,19 +253,19 @@ __global__ __launch_bounds__(THREADS, 1) void split_kernel(Args g, int tiles_m, 
         __bf16 *base = lds + stage * STAGE;
 #pragma unroll
         for (int v = 0; v < A_RUNS; ++v) {
-            bf16x8 p[3];
-            split3(ra[s][v], p[0], p[1], p[2]);
+            bR p[3];
+            split3<RUN>(ra[s][v], p[0], p[1], p[2]);
 #pragma unroll
             for (int q = 0; q < PARTS; ++q)
-                *(bf16x8 *)(base + q * A_PART + slot(a_row[v], a_h[v])) = p[q];
+                *(bR *)(base + q * A_PART + slot(a_row[v], a_k[v])) = p[q];
         }
 #pragma unroll
         for (int v = 0; v < B_RUNS; ++v) {
-            bf16x8 p[3];
-            split3(rb[s][v], p[0], p[1], p[2]);
+            bR p[3];
+            split3<RUN>(rb[s][v], p[0], p[1], p[2]);
 #pragma unroll
             for (int q = 0; q < PARTS; ++q)
-                *(bf16x8 *)(base + PARTS * A_PART + q * B_PART + slot(b_col[v], b_h[v])) = p[q];
+                *(bR *)(base + PARTS * A_PART + q * B_PART + slot(b_col[v], b_k[v])) = p[q];
         }
     };
 
@@ -191,17 +273,20 @@ __global__ __launch_bounds__(THREADS, 1) void split_kernel(Args g, int tiles_m, 
         bf16x8 a[PARTS][TM];
         bf16x8 b[PARTS][TN];
     };
+    auto read_b = [&](bf16x8 *b, const __bf16 *base, int q) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            b[j] = *(const bf16x8 *)(base + PARTS * A_PART + q * B_PART +
+                                     slot(wn * WN + 32 * j + lr, 8 * lh));
+    };
     auto read_frag = [&](Frag &f, int stage) {
         const __bf16 *base = lds + stage * STAGE;
 #pragma unroll
         for (int q = 0; q < PARTS; ++q) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                f.a[q][i] = *(const bf16x8 *)(base + q * A_PART + slot(wm * WM + 32 * i + lr, lh));
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                f.b[q][j] = *(const bf16x8 *)(base + PARTS * A_PART + q * B_PART +
-                                              slot(wn * WN + 32 * j + lr, lh));
+                f.a[q][i] = *(const bf16x8 *)(base + q * A_PART + slot(wm * WM + 32 * i + lr, 8 * lh));
+            if constexpr (T::FRAGS > 0) read_b(f.b[q], base, q);
         }
     };
     f32x16 acc[TM][TN];
@@ -220,6 +305,27 @@ __global__ __launch_bounds__(THREADS, 1) void split_kernel(Args g, int tiles_m, 
                         f.a[PP[t][0]][i], f.b[PP[t][1]][j], acc[i][j], 0, 0, 0);
     };
 
+    // FRAGS == 0: the parts of B in turn, each followed by its products,
+    // (0,2), (1,1), (0,1), (2,0), (1,0), (0,0).
+    auto multiply_stream = [&](const Frag &f, int stage) {
+        const __bf16 *base = lds + stage * STAGE;
+#pragma unroll
+        for (int q = PARTS - 1; q >= 0; --q) {
+            bf16x8 b[TN];
+            read_b(b, base, q);
+#pragma unroll
+            for (int p = 0; p + q < PARTS; ++p) {
+                const int pa = q == 0 ? PARTS - 1 - p : p;  // with B part 0, A parts 2, 1, 0
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[pa][i], b[j],
+                                                                            acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+
     const int nw = (K + BK - 1) / BK;   // windows
     const int nfull = K / BK;           // windows with every k < K
     auto fetch_any = [&](int s, int w) {
@@ -230,48 +336,57 @@ __global__ __launch_bounds__(THREADS, 1) void split_kernel(Args g, int tiles_m, 
         }
     };
 
-    // Prologue: windows 0 and 1 to LDS, windows 2 and 3 to the register slots.
+    // Prologue: windows 0 and 1 to LDS, windows 2 .. 1 + SLOTS to the register slots.
+    constexpr int AHEAD = 2 + T::SLOTS;  // distance from the computed to the fetched window
     fetch_any(0, 0);
     stash(0, 0);
     if (1 < nw) {
-        fetch_any(1, 1);
-        stash(1, 1);
+        fetch_any(0, 1);
+        stash(0, 1);
     }
-    fetch_any(0, 2);
-    fetch_any(1, 3);
+#pragma unroll
+    for (int s2 = 0; s2 < T::SLOTS; ++s2) fetch_any(s2, 2 + s2);
     __syncthreads();
-    Frag frag[2];
-    read_frag(frag[0], 0);
+    Frag frag[T::FRAGS == 2 ? 2 : 1];
+    if constexpr (T::FRAGS == 2) read_frag(frag[0], 0);
 
-    // Window w: its fragments are in frag[w & 1]; LDS holds w and w + 1; the
-    // register slots hold w + 2 (slot w & 1) and w + 3.
-    auto body = [&](auto steady_tag, auto slot_tag, int w) {
+    // Window w (parity P = w & 1): LDS holds w and w + 1; register slot
+    // (w + 2) % SLOTS holds w + 2; with two fragment buffers, frag[P] holds w's.
+    auto body = [&](auto steady_tag, auto parity_tag, int w) {
         constexpr bool STEADY = decltype(steady_tag)::value;
-        constexpr int S = decltype(slot_tag)::value;
+        constexpr int P = decltype(parity_tag)::value;
+        constexpr int S = P % T::SLOTS;
         const int cur = w % STAGES;
         const int next = cur + 1 == STAGES ? 0 : cur + 1;
         const int fill = cur == 0 ? STAGES - 1 : cur - 1;
-        read_frag(frag[S ^ 1], next);  // unused after the last window; keeps waits exact
+        if constexpr (T::FRAGS == 2) {
+            read_frag(frag[P ^ 1], next);  // unused after the last window; keeps waits exact
+        } else {
+            read_frag(frag[0], cur);
+        }
         if (STEADY || w + 2 < nw) stash(S, fill);
         if constexpr (STEADY) {
-            fetch(std::true_type{}, S, w + 4);
+            fetch(std::true_type{}, S, w + AHEAD);
         } else {
-            fetch_any(S, w + 4);
+            fetch_any(S, w + AHEAD);
         }
-        multiply(frag[S]);
-        if constexpr (STEADY) {
-            // MFMAs spread between the memory operations (see interleave()).
-            interleave<6 * TM * TN, PARTS * (TM + TN), PARTS * (A_RUNS + B_RUNS),
-                       2 * A_RUNS + 8 * B_RUNS>();
+        if constexpr (T::FRAGS == 0) {
+            multiply_stream(frag[0], cur);
+        } else {
+            multiply(frag[T::FRAGS == 2 ? P : 0]);
+        }
+        if constexpr (STEADY && T::FRAGS > 0) {
+            interleave_split<6 * TM * TN, PARTS * (TM + TN), PARTS * (A_RUNS + B_RUNS),
+                             RUN / 4 * A_RUNS + RUN * B_RUNS, 4>();
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
     };
 
     int w = 0;
-    // Steady state: windows up to w + 5 all full, two at a time (the register slot
-    // of a window is static in the unrolled body).
-    for (; w + 5 < nfull; w += 2) {
+    // Steady state: every window fetched in the pair is full; two windows at a
+    // time, so that slots and fragment buffers are static in the unrolled body.
+    for (; w + 1 + AHEAD < nfull; w += 2) {
         body(std::true_type{}, std::integral_constant<int, 0>{}, w);
         body(std::true_type{}, std::integral_constant<int, 1>{}, w + 1);
     }
@@ -300,16 +415,43 @@ __global__ __launch_bounds__(THREADS, 1) void split_kernel(Args g, int tiles_m, 
     }
 }
 
+template <class T>
+hipError_t launch_split_tile(const Problem &p, hipStream_t s) {
+    if (p.ta || p.tb) return hipErrorInvalidValue;
+    const int64_t tiles_m = (p.M + T::BM - 1) / T::BM;
+    const int64_t tiles_n = (p.N + T::BN - 1) / T::BN;
+    if (tiles_m * tiles_n > INT32_MAX) return hipErrorInvalidValue;
+    const Args g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
+    return launch(split_kernel<T>, dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0, s, g,
+                  (int)tiles_m, (int)tiles_n);
+}
+
+// 256 x 256 blocks of eight waves (two per SIMD) with 128 x 64 of C each; B
+// parts read one at a time: large products.
+using SplitHuge = Tile<256, 256, 128, 64, 3, 1, 8, 0, 1, 8>;
+// 256 x 128 blocks of eight waves with 64 x 64 each, runs of 4 k: grids of about
+// one block per CU, such as 2048 x 3072.
+using SplitMid = Tile<256, 128, 64, 64, 3, 1, 8, 1, 1, 4>;
+
 }  // namespace split
 
+// The busiest CU works through ceil(blocks / CUs) blocks; each costs BM*BN / e
+// with e the configuration's measured throughput at 8192^3 (233 and 208
+// TFLOP/s).  The cheaper estimate wins.
 hipError_t launch_split(const Problem &p, hipStream_t s) {
-    if (p.ta || p.tb) return hipErrorInvalidValue;
-    const int64_t tiles_m = (p.M + split::BM - 1) / split::BM;
-    const int64_t tiles_n = (p.N + split::BN - 1) / split::BN;
-    if (tiles_m * tiles_n > INT32_MAX) return hipErrorInvalidValue;
-    const split::Args g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
-    return launch(split::split_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(split::THREADS), 0,
-                  s, g, (int)tiles_m, (int)tiles_n);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    auto cost = [&](int bm, int bn, double e) {
+        const double blocks = (double)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+        return std::ceil(blocks / cus) * bm * bn / e;
+    };
+    if (cost(split::SplitHuge::BM, split::SplitHuge::BN, 233.0) <=
+        cost(split::SplitMid::BM, split::SplitMid::BN, 208.0))
+        return split::launch_split_tile<split::SplitHuge>(p, s);
+    return split::launch_split_tile<split::SplitMid>(p, s);
 }
 
 }  // namespace sgemm
