@@ -226,6 +226,11 @@ CONFIGS = [("c1", 512, 512, 512, "normal", 1), ("c2", 1024, 1024, 1024, "normal"
            ("c4b", 1, 4096, 4096, "uniform_pm1", 5), ("c5", 8192, 8192, 8192, "normal", 6)]
 
 
+def _check(status, sg):
+    if status != 0:
+        raise sg.SgemmError(status)
+
+
 def gpu_sclk(torch):
     """Current shader clock level of device 0 as the driver reports it, or None."""
     try:
@@ -310,6 +315,15 @@ def config_report(torch, sg, args):
                               "pct_hbm_peak": round(100 * nbytes / (rmed * 1e-3) / 1e9 /
                                                     PEAK_HBM_GBS, 2)}
             del bufs
+        if algo == sg.ALGO_MFMA:
+            sms = timed_launches(torch, stream, lambda: _check(sg.sgemm_f32_algo(
+                M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, stream.cuda_stream,
+                sg.ALGO_BF16X6), sg))
+            smed = statistics.median(sms)
+            rec["bf16x6"] = {"kernel_ms_median": round(smed, 5),
+                             "tflops": round(flops / (smed * 1e-3) / 1e12, 3),
+                             "pct_fp32_peak": round(100 * flops / (smed * 1e-3) / 1e12 /
+                                                    PEAK_FP32_TFLOPS, 2)}
         if args.cpu_seconds > 0:
             rec["host_blocked"] = cpu_blocked(A, B, M, N, K, reps=3 if M * N * K < 1e10 else 1)
         if name in ("c1", "c2") and args.cpu_seconds > 0:
@@ -492,6 +506,18 @@ def main(argv=None):
         gbs = algorithmic_bytes(M, N, K) / (kavg * 1e-3) / 1e9
         rec["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    if layout == (0, 0) and algo == sg.ALGO_AUTO and M > 8 and N > 8:
+        # the same product on the split-precision rung (fp32 accuracy on the bf16
+        # matrix cores), reported beside the fp32 result, never as the value
+        _, sms = time_product(torch, sg, M, N, K, dA, dB, dC, sg.ALGO_BF16X6, args.steps,
+                              args.warmup)
+        savg = sum(sms) / len(sms)
+        rec["bf16x6"] = {"kernel_ms_avg": round(savg, 4),
+                         "kernel_tflops": round(flops / (savg * 1e-3) / 1e12, 3),
+                         "pct_fp32_peak": round(100 * flops / (savg * 1e-3) / 1e12 /
+                                                PEAK_FP32_TFLOPS, 2),
+                         "note": "fp32 product on bf16 matrix cores, operands split into "
+                                 "three bf16 parts (six part products), fp32 accumulation"}
     del dA, dB, dC
     if not args.no_also:
         m2, n2, k2 = 2048, 3072, 4096
