@@ -7,8 +7,10 @@
 // of A in flight per element of B, and splits K across the work-items of a
 // work-group (k = slot, slot + S, slot + 2S, ...), followed by a fixed-order
 // pairwise reduction in LDS, so results are reproducible and no atomics are
-// needed.  Up to 1024 work-items per group keep enough 16-byte loads in flight
-// per CU to cover HBM latency.
+// needed.  Each work-group owns a strip of 4*LPR columns; with 16 columns (64
+// bytes of a row) two work-groups share every 128-byte line, so strips are
+// assigned XCD by XCD: neighbouring strips run on the same XCD and a line comes
+// through its L2 once, not once per XCD.
 #include <type_traits>
 
 #include "internal.h"
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
 
     const int tid = threadIdx.x;
     const int q = tid % LPR, slot = tid / LPR;
-    const int n0 = blockIdx.x * CW;
+    const int n0 = xcd_remap(blockIdx.x, gridDim.x) * CW;
     const int n = n0 + 4 * q;
     const bool vec = n + 3 < N;
 
@@ -158,8 +160,9 @@ hipError_t launch_skinny(const Problem &p, hipStream_t s) {
         q.A = p.A + (int64_t)r0 * p.lda;
         q.C = p.C + (int64_t)r0 * p.ldc;
         hipError_t e;
-        // Fewer rows leave room for more work-items (loads in flight) per group.
-        if (q.M == 1) e = launch_rows<1, 1024>(q, s);
+        // Group sizes measured on 1..8 x 4096 x 4096 with B resident in the
+        // Infinity Cache and streamed from HBM.
+        if (q.M == 1) e = launch_rows<1, 256>(q, s);
         else if (q.M == 2) e = launch_rows<2, 512>(q, s);
         else if (q.M <= 4) e = launch_rows<4, 512>(q, s);
         else e = launch_rows<8, 256>(q, s);
