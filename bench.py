@@ -285,11 +285,13 @@ def config_report(torch, sg, args):
         kms = timed_launches(torch, stream, launch)
         med = statistics.median(kms)
         flops, nbytes = algorithmic_flops(M, N, K), algorithmic_bytes(M, N, K)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        _, m_main, n_main = sg.sgemm_f32_auto_plan(0, 0, M, N, K, cus)
         rec = {"config": name, "shape": [M, N, K], "dist": dist, "seed": seed,
                "algo": sg.sgemm_f32_algo_name(algo),
                "tile": sg.sgemm_f32_mfma_tile_name(sg.sgemm_f32_mfma_select(
-                   M, N, K, torch.cuda.get_device_properties(0).multi_processor_count))
-               if algo == sg.ALGO_MFMA else None,
+                   m_main, n_main, K, cus)) if algo == sg.ALGO_MFMA else None,
+               "blocks_cover": [m_main, n_main],
                "kernel_ms_median": round(med, 5), "kernel_ms_mean": round(sum(kms) / len(kms), 5),
                "kernel_ms_min": round(min(kms), 5), "launches": len(kms),
                "tflops": round(flops / (med * 1e-3) / 1e12, 3),

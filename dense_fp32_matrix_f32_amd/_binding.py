@@ -34,7 +34,7 @@ OP_T = 1
 EXPORTED = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name",
             "sgemm_f32_ex", "sgemm_f32_ex_algo", "sgemm_f32_colmajor",
             "sgemm_f32_mfma_tiles", "sgemm_f32_mfma_tile_name", "sgemm_f32_mfma_select",
-            "sgemm_f32_mfma_tile", "sgemm_f32_ex_mfma_tile")
+            "sgemm_f32_mfma_tile", "sgemm_f32_ex_mfma_tile", "sgemm_f32_auto_plan")
 
 _lib = None
 
@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
         l.sgemm_f32_ex_algo.restype = i
         l.sgemm_f32_ex_mfma_tile.argtypes = ex_args + [i]
         l.sgemm_f32_ex_mfma_tile.restype = i
+        ip = ctypes.POINTER(i)
+        l.sgemm_f32_auto_plan.argtypes = [i, i, i, i, i, i, ip, ip]
+        l.sgemm_f32_auto_plan.restype = i
         _lib = l
     return _lib
 
@@ -125,6 +128,16 @@ def sgemm_f32_mfma_tile_name(tile: int):
 def sgemm_f32_mfma_select(M, N, K, compute_units=256) -> int:
     """Configuration id the matrix-core rung uses for this shape (host-only)."""
     return lib().sgemm_f32_mfma_select(M, N, K, compute_units)
+
+
+def sgemm_f32_auto_plan(transa, transb, M, N, K, compute_units=256):
+    """(algorithm id, m_main, n_main) of the automatic choice (host-only); the id is
+    -1 for invalid arguments.  Columns [n_main, N) and then rows [m_main, M) of
+    columns [0, n_main) go to a second kernel sized for that strip."""
+    m, n = ctypes.c_int(-1), ctypes.c_int(-1)
+    algo = lib().sgemm_f32_auto_plan(transa, transb, M, N, K, compute_units,
+                                     ctypes.byref(m), ctypes.byref(n))
+    return algo, m.value, n.value
 
 
 def sgemm_f32_mfma_tile(M, N, K, A, lda, B, ldb, C, ldc, stream=0, tile=0) -> int:

@@ -53,8 +53,12 @@ hipError_t launch_mfma(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_tile(const Problem &p, hipStream_t s, int tile);
 int mfma_tile_count();
 const char *mfma_tile_name(int tile);
-// The configuration launch_mfma() uses for this shape on `cus` compute units.
+// The configuration launch_mfma() uses for this shape on `cus` compute units,
+// and the cost model's time for it in microseconds.
 int mfma_select(int M, int N, int K, int cus);
+double mfma_model_us(int M, int N, int K, int cus);
+// Compute units of the current device (256 if the query fails).
+int compute_units();
 // The fp32 product on the bf16 matrix cores with three-part operand splitting
 // (untransposed operands only).
 hipError_t launch_split(const Problem &p, hipStream_t s);

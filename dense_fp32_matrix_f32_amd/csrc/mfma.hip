@@ -49,7 +49,7 @@ static_assert(kTiles[4].bm == TileSmall::BM && kTiles[4].bn == TileSmall::BN, "r
 static_assert(kTiles[5].bm == TileSplit64::BM && kTiles[5].bn == TileSplit64::BN, "row 5");
 static_assert(kTiles[6].bm == TileTiny::BM && kTiles[6].bn == TileTiny::BN, "row 6");
 
-static int compute_units() {
+int compute_units() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -58,8 +58,9 @@ static int compute_units() {
     return cus;
 }
 
-// Index into kTiles of the configuration the model prefers for this shape.
-static int choose_tile(int M, int N, int K, int cus) {
+// Index into kTiles of the configuration the model prefers for this shape, and
+// its modelled time in microseconds.
+static int choose_tile(int M, int N, int K, int cus, double *model_us = nullptr) {
     int best = 0;
     double best_us = 0;
     for (int i = 0; i < kTileCount; ++i) {
@@ -76,6 +77,7 @@ static int choose_tile(int M, int N, int K, int cus) {
             best_us = us;
         }
     }
+    if (model_us) *model_us = best_us;
     return best;
 }
 
@@ -95,6 +97,12 @@ const char *mfma_tile_name(int tile) {
 }
 
 int mfma_select(int M, int N, int K, int cus) { return choose_tile(M, N, K, cus > 0 ? cus : 256); }
+
+double mfma_model_us(int M, int N, int K, int cus) {
+    double us = 0;
+    choose_tile(M, N, K, cus > 0 ? cus : 256, &us);
+    return us;
+}
 
 hipError_t launch_mfma_tile(const Problem &p, hipStream_t s, int tile) {
     if (tile < 0 || tile >= kTileCount) return hipErrorInvalidValue;

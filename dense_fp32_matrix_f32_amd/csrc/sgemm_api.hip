@@ -56,6 +56,98 @@ int choose(int transa, int transb, int M, int N, int K) {
     return SGEMM_F32_ALGO_MFMA;
 }
 
+// Automatic choice for the products the matrix cores take.  When N lies a few
+// columns past a multiple of 32 (M a few rows), those columns (rows) need a whole
+// extra column (row) of blocks of C, which can add a round of blocks on the CUs
+// for a sliver of work (4095 x 4097: 726 blocks of 192 x 128 for 4095 x 4096
+// plus one column).  The product is then split: the blocks cover the leading
+// multiple of 32 and the strip that is left goes to a kernel sized for it (the
+// streaming kernels for untransposed operands, the matrix cores otherwise), when
+// the cost model of the tile table says the launches together finish sooner.
+// Every element of C is still computed whole by exactly one kernel.
+constexpr int kPeelMax = 8;    // widest strip split off
+constexpr double kStreamBytesPerUs = 2.5e6;  // streaming kernels on small strips
+constexpr double kStreamLaunchUs = 4.0;
+
+// Modelled time of a rows x cols strip over the whole k range.
+double strip_us(const Problem &p, int rows, int cols, int cus) {
+    if (!p.ta && !p.tb) {
+        const double bytes =
+            4.0 * ((double)rows * p.K + (double)p.K * cols + (double)rows * cols);
+        return kStreamLaunchUs + bytes / kStreamBytesPerUs;
+    }
+    return sgemm::mfma_model_us(rows, cols, p.K, cus);
+}
+
+hipError_t launch_strip(const Problem &q, hipStream_t s) {
+    if (!q.ta && !q.tb) {
+        if (q.M <= kPeelMax) return sgemm::launch_skinny(q, s);
+        return sgemm::launch_skinny_n(q, s);
+    }
+    return sgemm::launch_mfma(q, s);
+}
+
+// Columns [n0, N) of op(B) and C, all rows.
+Problem column_strip(const Problem &p, int n0) {
+    Problem q = p;
+    q.N = p.N - n0;
+    q.B = p.tb ? p.B + (int64_t)n0 * p.ldb : p.B + n0;
+    q.C = p.C + n0;
+    return q;
+}
+
+// Rows [m0, M) of op(A) and C, columns [0, n_end).
+Problem row_strip(const Problem &p, int m0, int n_end) {
+    Problem q = p;
+    q.M = p.M - m0;
+    q.N = n_end;
+    q.A = p.ta ? p.A + m0 : p.A + (int64_t)m0 * p.lda;
+    q.C = p.C + (int64_t)m0 * p.ldc;
+    return q;
+}
+
+// Extents of the part of C that the blocks cover; the rest (columns
+// [n_main, N), then rows [m_main, M) of columns [0, n_main)) goes to strips.
+struct Split {
+    int m_main, n_main;
+};
+
+Split plan_split(const Problem &p, int cus) {
+    Split full{p.M, p.N};
+    const int rn = p.N % 32, rm = p.M % 32;
+    const bool cut_n = p.N >= 64 && rn >= 1 && rn <= kPeelMax;
+    const bool cut_m = p.M >= 64 && rm >= 1 && rm <= kPeelMax;
+    if (!cut_n && !cut_m) return full;
+    const double full_us = sgemm::mfma_model_us(p.M, p.N, p.K, cus);
+    Split best = full;
+    double best_us = full_us;
+    // bit 0 splits off the last rn columns, bit 1 the last rm rows
+    for (int plan = 1; plan < 4; ++plan) {
+        const bool pn = plan & 1, pm = plan & 2;
+        if ((pn && !cut_n) || (pm && !cut_m)) continue;
+        const Split sp{pm ? p.M - rm : p.M, pn ? p.N - rn : p.N};
+        double us = sgemm::mfma_model_us(sp.m_main, sp.n_main, p.K, cus);
+        if (pn) us += strip_us(p, p.M, rn, cus);
+        if (pm) us += strip_us(p, rm, sp.n_main, cus);
+        if (us < best_us) {
+            best = sp;
+            best_us = us;
+        }
+    }
+    return best_us <= 0.97 * full_us ? best : full;
+}
+
+hipError_t launch_auto_mfma(const Problem &p, hipStream_t s) {
+    const Split sp = plan_split(p, sgemm::compute_units());
+    Problem main = p;
+    main.M = sp.m_main;
+    main.N = sp.n_main;
+    hipError_t e = sgemm::launch_mfma(main, s);
+    if (e == hipSuccess && sp.n_main < p.N) e = launch_strip(column_strip(p, sp.n_main), s);
+    if (e == hipSuccess && sp.m_main < p.M) e = launch_strip(row_strip(p, sp.m_main, sp.n_main), s);
+    return e;
+}
+
 bool handles_transposes(int algo) {
     return algo == SGEMM_F32_ALGO_AUTO || algo == SGEMM_F32_ALGO_NAIVE ||
            algo == SGEMM_F32_ALGO_LDS_TILED || algo == SGEMM_F32_ALGO_MFMA;
@@ -111,6 +203,25 @@ extern "C" int sgemm_f32_select(int M, int N, int K, const float *A, int lda, co
     return choose(SGEMM_F32_OP_N, SGEMM_F32_OP_N, M, N, K);
 }
 
+extern "C" int sgemm_f32_auto_plan(int transa, int transb, int M, int N, int K,
+                                   int compute_units, int *m_main, int *n_main) {
+    if ((transa != SGEMM_F32_OP_N && transa != SGEMM_F32_OP_T) ||
+        (transb != SGEMM_F32_OP_N && transb != SGEMM_F32_OP_T) || M < 0 || N < 0 || K < 0 ||
+        m_main == nullptr || n_main == nullptr)
+        return -1;
+    const int algo = choose(transa, transb, M, N, K);
+    Split sp{M, N};
+    if (algo == SGEMM_F32_ALGO_MFMA && M > 0 && N > 0 && K > 0) {
+        Problem p{M, N, K, nullptr, 1, nullptr, 1, nullptr, 1};
+        p.ta = transa == SGEMM_F32_OP_T;
+        p.tb = transb == SGEMM_F32_OP_T;
+        sp = plan_split(p, compute_units > 0 ? compute_units : 256);
+    }
+    *m_main = sp.m_main;
+    *n_main = sp.n_main;
+    return algo;
+}
+
 extern "C" hipError_t sgemm_f32_ex_algo(int transa, int transb, int M, int N, int K, float alpha,
                                         const float *A, int lda, const float *B, int ldb,
                                         float beta, float *C, int ldc, hipStream_t stream,
@@ -122,7 +233,10 @@ extern "C" hipError_t sgemm_f32_ex_algo(int transa, int transb, int M, int N, in
     if (trivial(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, &st))
         return st;
     const Problem p = problem(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    if (algo == SGEMM_F32_ALGO_AUTO) algo = choose(transa, transb, M, N, K);
+    if (algo == SGEMM_F32_ALGO_AUTO) {
+        algo = choose(transa, transb, M, N, K);
+        if (algo == SGEMM_F32_ALGO_MFMA) return launch_auto_mfma(p, stream);
+    }
     switch (algo) {
     case SGEMM_F32_ALGO_NAIVE: return sgemm::launch_naive(p, stream);
     case SGEMM_F32_ALGO_LDS_TILED: return sgemm::launch_lds_tiled(p, stream);

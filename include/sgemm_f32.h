@@ -139,7 +139,8 @@ const char *sgemm_f32_algo_name(int algo);
  * either storage order; VALU_REGBLOCK, SKINNY and SKINNY_N accept only
  * SGEMM_F32_OP_N for both operands (hipErrorInvalidValue otherwise).  AUTO
  * uses the SKINNY and SKINNY_N rules of sgemm_f32() for untransposed operands
- * and MFMA for every other product.
+ * and MFMA for every other product; see sgemm_f32_auto_plan() for how AUTO may
+ * split an MFMA product into blocks and an edge strip.
  *
  * sgemm_f32_colmajor() takes the same arguments with every array column-major,
  * as in the reference BLAS sgemm: A is M x K (transa = N, lda >= max(1,M)) or
@@ -202,6 +203,26 @@ hipError_t sgemm_f32_ex_mfma_tile(int transa, int transb, int M, int N, int K, f
                                   const float *B, int ldb, float beta,
                                   float *C, int ldc,
                                   hipStream_t stream, int tile);
+
+/*
+ * How SGEMM_F32_ALGO_AUTO runs an M x N x K product with the given storage
+ * orders on a device with `compute_units` CUs (<= 0 means 256); host-only, no
+ * HIP call.  Returns the algorithm id AUTO resolves to (as sgemm_f32_select()
+ * for untransposed operands), or -1 for invalid arguments.  *m_main and
+ * *n_main receive the extent of C that the chosen algorithm covers; when the
+ * algorithm is SGEMM_F32_ALGO_MFMA and N (M) lies 1 to 8 past a multiple of
+ * 32, AUTO may leave the last N % 32 columns (M % 32 rows) to a second kernel
+ * sized for that strip (the SKINNY_N or SKINNY kernel for untransposed
+ * operands, the matrix-core rung otherwise) when the tile cost model says the
+ * two launches finish sooner: the columns [n_main, N) of all rows, then the
+ * rows [m_main, M) of columns [0, n_main).  The blocks of the main part use
+ * configuration sgemm_f32_mfma_select(m_main, n_main, K, compute_units).
+ * Every element of C is computed by exactly one kernel, so results are still
+ * reproducible run to run; they match the forced MFMA rung within the error
+ * bound, not bit for bit, in the strip.
+ */
+int sgemm_f32_auto_plan(int transa, int transb, int M, int N, int K, int compute_units,
+                        int *m_main, int *n_main);
 
 #ifdef __cplusplus
 }

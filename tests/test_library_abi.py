@@ -153,6 +153,42 @@ def test_mfma_tile_selection():
     assert 0 <= sg.sgemm_f32_mfma_select(8192, 8192, 8192, 80) < sg.sgemm_f32_mfma_tiles()
 
 
+def test_auto_plan_splits_edge_strips():
+    # 4095 x 4097 x 1023: one column past 4096 would add a round of blocks; the
+    # blocks cover 4095 x 4096 and the last column goes to a strip kernel.
+    for ta in (0, 1):
+        for tb in (0, 1):
+            assert sg.sgemm_f32_auto_plan(ta, tb, 4095, 4097, 1023, 256) == (sg.ALGO_MFMA, 4095,
+                                                                             4096)
+    assert sg.sgemm_f32_auto_plan(0, 0, 4097, 4095, 1023, 256) == (sg.ALGO_MFMA, 4096, 4095)
+    assert sg.sgemm_f32_auto_plan(0, 0, 3073, 2050, 511, 256) == (sg.ALGO_MFMA, 3072, 2048)
+    assert sg.sgemm_f32_auto_plan(1, 1, 2049, 4097, 1023, 256) == (sg.ALGO_MFMA, 2048, 4096)
+    # multiples of 32 (every workload but the ragged one) are never split
+    for shape in [(512, 512, 512), (1024, 1024, 1024), (2048, 3072, 4096), (8192, 8192, 8192)]:
+        assert sg.sgemm_f32_auto_plan(0, 0, *shape, 256) == (sg.ALGO_MFMA, shape[0], shape[1])
+    # strips of more than 8, and small products, stay whole
+    assert sg.sgemm_f32_auto_plan(0, 0, 4095, 4105, 1023, 256) == (sg.ALGO_MFMA, 4095, 4105)
+    assert sg.sgemm_f32_auto_plan(0, 0, 40, 41, 1023, 256) == (sg.ALGO_MFMA, 40, 41)
+    # the streaming rungs cover the whole product
+    assert sg.sgemm_f32_auto_plan(0, 0, 1, 4097, 4096, 256) == (sg.ALGO_SKINNY, 1, 4097)
+    assert sg.sgemm_f32_auto_plan(0, 0, 4097, 3, 4096, 256) == (sg.ALGO_SKINNY_N, 4097, 3)
+    assert sg.sgemm_f32_auto_plan(1, 0, 1, 4097, 4096, 256) == (sg.ALGO_MFMA, 1, 4097)
+    # invalid arguments
+    assert sg.sgemm_f32_auto_plan(2, 0, 8, 8, 8, 256)[0] == -1
+    assert sg.sgemm_f32_auto_plan(0, 0, -1, 8, 8, 256)[0] == -1
+    # any plan leaves at most 8 columns and rows, at the high end
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        M, N, K = (int(x) for x in rng.integers(1, 6000, 3))
+        ta, tb = (int(x) for x in rng.integers(0, 2, 2))
+        algo, m, n = sg.sgemm_f32_auto_plan(ta, tb, M, N, K, int(rng.integers(0, 300)))
+        assert algo >= 0
+        assert m in (M, M - M % 32) and n in (N, N - N % 32)
+        assert M - m <= 8 and N - n <= 8
+        if (m, n) != (M, N):
+            assert algo == sg.ALGO_MFMA and min(m, n) >= 56
+
+
 def test_mfma_tile_entry_validates():
     n = sg.sgemm_f32_mfma_tiles()
     for tile in (-1, n):
