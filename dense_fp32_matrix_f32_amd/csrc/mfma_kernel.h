@@ -9,7 +9,11 @@
 //     three LDS stages (later windows are written while the current one is read,
 //     so one barrier per window replaces the pages' two);
 //   * global -> LDS copies as 16-byte loads, issued a window ahead into
-//     registers so that their latency overlaps a whole window of math;
+//     registers so that their latency overlaps a whole window of math; when
+//     every lane's offset inside a block fits 32 bits (all but rows of more
+//     than about 2M floats), they are buffer loads whose base address is
+//     uniform (SGPRs, advanced once per window) and whose per-lane offsets
+//     stay fixed, so no vector instruction is spent on addresses;
 //   * the operand fragments of the next 8-wide k step are read from LDS while
 //     the MFMAs of the current step run; with three stages this reaches across
 //     the window boundary, so the barrier does not leave the matrix cores idle;
@@ -95,6 +99,15 @@ __device__ __forceinline__ f32x4 load16(const float *p) {
     return v;
 }
 
+// 16-byte load at byte offset `off` from the uniform address `base`, through a
+// buffer resource (no range limit; the caller keeps every access inside its
+// matrix).
+__device__ __forceinline__ f32x4 load16_at(const char *base, uint32_t off) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, -1, 0x00020000);
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // Scheduling hint for one basic block holding MF MFMAs, DSR LDS reads, DSW LDS
 // writes and VMR global loads: each memory instruction is placed right after an
 // MFMA, so a single wave keeps its matrix core fed while it issues them.  When
@@ -160,10 +173,11 @@ struct MfmaTile {
 
 // A tile configuration with the storage order of each operand: TA (op(A) is the
 // transpose of the stored K x M array) and TB (op(B) is the transpose of the
-// stored N x K array).
-template <class T, bool TA_, bool TB_>
+// stored N x K array); NARROW: every per-lane byte offset inside a block window
+// fits 32 bits (checked on the host by narrow_offsets()).
+template <class T, bool TA_, bool TB_, bool NARROW_ = true>
 struct Cfg : T {
-    static constexpr bool TA = TA_, TB = TB_;
+    static constexpr bool TA = TA_, TB = TB_, NARROW = NARROW_;
     static constexpr int PA = TA ? T::BM + T::PAD_B : T::BK + T::PAD_A;  // A window pitch
     static constexpr int PB = TB ? T::BK + T::PAD_A : T::BN + T::PAD_B;  // B window pitch
     static constexpr int A_STAGE = (TA ? T::BK : T::BM) * PA;
@@ -208,7 +222,9 @@ using Acc = f32x16[T::TM][T::TN];
 template <class T, bool KC, int ROWS_OR_COLS, int TOTAL, int VECS>
 struct Operand {
     static constexpr int Q = KC ? T::BK / 4 : ROWS_OR_COLS / 4;  // vectors per LDS row
-    const float *src[VECS];
+    const float *src[VECS];  // start of the vector in window 0 (when !NARROW)
+    const char *org;         // uniform: the block's first row (KC) or column
+    uint32_t off[VECS];      // byte offset of src[v] from org (when NARROW)
     int lds[VECS];
     int kofs[VECS];  // KC: k offset of the vector in the window; else its k row
     int pos[VECS];   // mn-contiguous: first column (m or n) of the vector
@@ -229,14 +245,27 @@ struct Operand {
             if constexpr (KC) {
                 const int gr = min(origin + row, extent - 1);
                 src[v] = X + (int64_t)gr * ld + q * 4;
+                org = (const char *)(X + (int64_t)origin * ld);
+                off[v] = (uint32_t)(((int64_t)(gr - origin) * ld + q * 4) * 4);
                 kofs[v] = q * 4;
                 pos[v] = 0;
             } else {
                 src[v] = X + (int64_t)row * ld + origin + q * 4;
+                org = (const char *)(X + origin);
+                off[v] = (uint32_t)(((int64_t)row * ld + q * 4) * 4);
                 kofs[v] = row;
                 pos[v] = origin + q * 4;
             }
             lds[v] = base + row * pitch + q * 4;
+        }
+    }
+
+    // Start of vector v in window 0.
+    __device__ __forceinline__ const float *at(int v) const {
+        if constexpr (T::NARROW) {
+            return (const float *)(org + off[v]);
+        } else {
+            return src[v];
         }
     }
 
@@ -246,12 +275,16 @@ struct Operand {
     __device__ __forceinline__ void fetch_full(int64_t k0, int64_t ld, int extent) {
 #pragma unroll
         for (int v = 0; v < VECS; ++v) {
-            if constexpr (KC) {
+            if constexpr (KC && T::NARROW) {
+                r[v] = load16_at(org + k0 * 4, off[v]);
+            } else if constexpr (KC) {
                 r[v] = load16(src[v] + k0);
+            } else if constexpr (INSIDE && T::NARROW) {
+                r[v] = load16_at(org + k0 * ld * 4, off[v]);
             } else if constexpr (INSIDE) {
                 r[v] = load16(src[v] + k0 * ld);
             } else {
-                const float *row = src[v] + k0 * ld - pos[v];
+                const float *row = at(v) + k0 * ld - pos[v];
                 r[v].x = row[min(pos[v] + 0, extent - 1)];
                 r[v].y = row[min(pos[v] + 1, extent - 1)];
                 r[v].z = row[min(pos[v] + 2, extent - 1)];
@@ -275,14 +308,14 @@ struct Operand {
         for (int v = 0; v < VECS; ++v) {
             if constexpr (KC) {
                 const int64_t kv = K - (k0 + kofs[v]);
-                const float *p = src[v] + k0;
+                const float *p = at(v) + k0;
                 r[v].x = kv > 0 ? p[0] : 0.0f;
                 r[v].y = kv > 1 ? p[1] : 0.0f;
                 r[v].z = kv > 2 ? p[2] : 0.0f;
                 r[v].w = kv > 3 ? p[3] : 0.0f;
             } else {
                 if (k0 + kofs[v] < K) {
-                    const float *row = src[v] + k0 * ld - pos[v];
+                    const float *row = at(v) + k0 * ld - pos[v];
                     r[v].x = row[min(pos[v] + 0, extent - 1)];
                     r[v].y = row[min(pos[v] + 1, extent - 1)];
                     r[v].z = row[min(pos[v] + 2, extent - 1)];
@@ -626,6 +659,18 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_kernel(GemmArgs g, in
     store_tile<C>(g, m0, n0, acc);
 }
 
+// True when every per-lane byte offset from a block's first row or column
+// stays below 2^31: (rows of one window - 1) * ld + one row of the window.
+template <class T, bool TA, bool TB>
+bool narrow_offsets(const Problem &p) {
+    auto fits = [](int64_t rows, int64_t ld, int64_t row_len) {
+        return ((rows - 1) * ld + row_len) * 4 < ((int64_t)1 << 31);
+    };
+    const bool a = TA ? fits(T::BK, p.lda, T::BM) : fits(T::BM, p.lda, T::BK);
+    const bool b = TB ? fits(T::BN, p.ldb, T::BK) : fits(T::BK, p.ldb, T::BN);
+    return a && b;
+}
+
 template <class T, bool TA, bool TB>
 hipError_t launch_tile(const Problem &p, hipStream_t s) {
     using C = Cfg<T, TA, TB>;
@@ -633,8 +678,12 @@ hipError_t launch_tile(const Problem &p, hipStream_t s) {
     const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
     if (tiles_m * tiles_n > INT32_MAX) return hipErrorInvalidValue;
     const GemmArgs g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
-    return launch(mfma_kernel<C>, dim3((unsigned)(tiles_m * tiles_n)), dim3(C::THREADS), 0, s, g,
-                  (int)tiles_m, (int)tiles_n);
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(C::THREADS);
+    if (narrow_offsets<T, TA, TB>(p))
+        return launch(mfma_kernel<Cfg<T, TA, TB, true>>, grid, block, 0, s, g, (int)tiles_m,
+                      (int)tiles_n);
+    return launch(mfma_kernel<Cfg<T, TA, TB, false>>, grid, block, 0, s, g, (int)tiles_m,
+                  (int)tiles_n);
 }
 
 // ---------------------------------------------------------------------------

@@ -68,3 +68,52 @@ def test_tile_k_zero_and_empty(tile):
     A, B = inputs(5, 6, 1, "normal", seed=1)
     C = _run(tile, A, B, 5, 6, 0)
     assert (C == 0).all()
+
+
+# Row strides so long that some lane of a block lies 2^31 bytes or more from the
+# block's first row or column: the kernels then address with 64-bit per-lane
+# pointers instead of 32-bit offsets from a uniform base.  (layout, M, N, K, lda,
+# ldb) with the stored arrays' row counts: A is M x lda (K x lda transposed), B is
+# K x ldb (N x ldb transposed).  Only the logical columns are copied to the GPU.
+WIDE = [
+    ((0, 0), 64, 48, 40, 2_200_000, 48),        # A k-contiguous, 255 rows apart
+    ((0, 0), 64, 48, 16, 40, 36_000_000),       # B n-contiguous, 15 rows apart
+    ((1, 1), 64, 48, 16, 36_000_000, 2_200_000),  # both transposed
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: f"{'T' if c[0][0] else 'N'}"
+                         f"{'T' if c[0][1] else 'N'}-lda{c[4]}-ldb{c[5]}")
+def test_wide_row_strides(case):
+    import numpy as np
+    import torch
+
+    import oracle
+    import synthgen
+    (ta, tb), M, N, K, lda, ldb = case
+    X = synthgen.matrix(M, K, seed=61, stream=0, dist="smallint")   # op(A)
+    Y = synthgen.matrix(K, N, seed=61, stream=1, dist="smallint")   # op(B)
+    As = np.ascontiguousarray(X.T if ta else X)
+    Bs = np.ascontiguousarray(Y.T if tb else Y)
+    exact, _ = oracle.sgemm(X, Y)
+    dev = {}
+    for name, S, ld in (("A", As, lda), ("B", Bs, ldb)):
+        buf = torch.zeros(S.shape[0] * ld, dtype=torch.float32, device="cuda")
+        buf.view(S.shape[0], ld)[:, :S.shape[1]] = torch.from_numpy(S).cuda()
+        dev[name] = buf
+    stream = torch.cuda.current_stream()
+    try:
+        for tile in (0, None):
+            C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+            log(f"[gpu] wide strides {'T' if ta else 'N'}{'T' if tb else 'N'} tile={tile} "
+                f"M={M} N={N} K={K} lda={lda} ldb={ldb}")
+            args = (ta, tb, M, N, K, 1.0, dev["A"].data_ptr(), lda, dev["B"].data_ptr(), ldb, 0.0,
+                    C.data_ptr(), N, stream.cuda_stream)
+            st = (sg.sgemm_f32_ex_mfma_tile(*args, tile) if tile is not None
+                  else sg.sgemm_f32_ex_algo(*args, sg.ALGO_MFMA))
+            assert st == 0
+            stream.synchronize()
+            assert np.array_equal(C.cpu().numpy().astype(np.float64), exact), f"tile {tile}"
+    finally:
+        del dev
+        torch.cuda.empty_cache()
