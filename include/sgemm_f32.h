@@ -30,7 +30,7 @@
  * kernels on `stream` (0 is the null stream) and returns without waiting.
  * The caller synchronises (hipStreamSynchronize, events, ...).
  *
- * Errors (returned, never fatal; nothing is enqueued on an error):
+ * Errors (returned, never fatal; an argument error enqueues nothing):
  *   hipErrorInvalidValue   M, N or K negative; lda < max(1,K); ldb < max(1,N);
  *                          ldc < max(1,N); A or B NULL when M*N*K > 0; C NULL
  *                          when M*N > 0; the written extent of C overlapping
