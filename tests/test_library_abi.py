@@ -161,7 +161,7 @@ def test_auto_plan_splits_edge_strips():
             assert sg.sgemm_f32_auto_plan(ta, tb, 4095, 4097, 1023, 256) == (sg.ALGO_MFMA, 4095,
                                                                              4096)
     assert sg.sgemm_f32_auto_plan(0, 0, 4097, 4095, 1023, 256) == (sg.ALGO_MFMA, 4096, 4095)
-    assert sg.sgemm_f32_auto_plan(0, 0, 3073, 2050, 511, 256) == (sg.ALGO_MFMA, 3072, 2048)
+    assert sg.sgemm_f32_auto_plan(0, 0, 4097, 4097, 1023, 256) == (sg.ALGO_MFMA, 4096, 4096)
     assert sg.sgemm_f32_auto_plan(1, 1, 2049, 4097, 1023, 256) == (sg.ALGO_MFMA, 2048, 4096)
     # multiples of 32 (every workload but the ragged one) are never split
     for shape in [(512, 512, 512), (1024, 1024, 1024), (2048, 3072, 4096), (8192, 8192, 8192)]:
