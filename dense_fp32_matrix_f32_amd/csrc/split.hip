@@ -170,7 +170,19 @@ struct Args {
     float alpha, beta;
 };
 
-template <class T>
+// Loads through a buffer resource whose base is the uniform address `base`, at
+// byte offset voff + soff (voff per lane, soff uniform); no range limit, the
+// caller keeps every access inside its matrix.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const char *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, -1, 0x00020000);
+}
+
+// NARROW: every per-lane byte offset from the block's first row of A or first
+// column of B stays below 2^31 (checked on the host), so full windows are read
+// with buffer loads: uniform bases advanced once per window, fixed lane offsets,
+// and for B the k rows of a run as uniform offsets, with no vector address
+// arithmetic.  Otherwise every lane keeps 64-bit pointers.
+template <class T, bool NARROW>
 __global__ __launch_bounds__(T::THREADS, T::OCC) void split_kernel(Args g, int tiles_m,
                                                                   int tiles_n) {
     constexpr int BM = T::BM, BN = T::BN, WM = T::WM, WN = T::WN, TM = T::TM, TN = T::TN;
@@ -191,22 +203,30 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void split_kernel(Args g, int t
     typedef typename Run<RUN>::f fR;
     typedef typename Run<RUN>::b bR;
     const float *a_src[A_RUNS];
+    uint32_t a_off[A_RUNS];  // byte offset of a_src[v] from a_org
     int a_row[A_RUNS], a_k[A_RUNS];
+    const char *a_org = (const char *)(g.A + (int64_t)m0 * g.lda);
 #pragma unroll
     for (int v = 0; v < A_RUNS; ++v) {
         const int c = tid + v * THREADS;  // run c: row c / RPR, k RUN * (c % RPR)
         a_row[v] = c / RPR;
         a_k[v] = RUN * (c % RPR);
-        a_src[v] = g.A + (int64_t)min(m0 + a_row[v], M - 1) * g.lda + a_k[v];
+        const int64_t e = (int64_t)(min(m0 + a_row[v], M - 1) - m0) * g.lda + a_k[v];
+        a_src[v] = g.A + (int64_t)m0 * g.lda + e;
+        a_off[v] = (uint32_t)(e * 4);
     }
     const float *b_src[B_RUNS];
+    uint32_t b_off[B_RUNS];  // byte offset of b_src[v] from b_org
     int b_col[B_RUNS], b_k[B_RUNS];
+    const char *b_org = (const char *)(g.B + n0);
 #pragma unroll
     for (int v = 0; v < B_RUNS; ++v) {
         const int c = tid + v * THREADS;  // run c: column c % BN, k RUN * (c / BN)
         b_col[v] = c % BN;
         b_k[v] = RUN * (c / BN);
-        b_src[v] = g.B + (int64_t)b_k[v] * g.ldb + min(n0 + b_col[v], N - 1);
+        const int64_t e = (int64_t)b_k[v] * g.ldb + (min(n0 + b_col[v], N - 1) - n0);
+        b_src[v] = g.B + n0 + e;
+        b_off[v] = (uint32_t)(e * 4);
     }
 
     // Register slots of fetched windows.
@@ -216,9 +236,33 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void split_kernel(Args g, int t
     auto fetch = [&](auto full_tag, int s, int w) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int64_t k0 = (int64_t)w * BK;
+        if constexpr (FULL && NARROW) {
+            const __amdgpu_buffer_rsrc_t ra_ = rsrc_at(a_org + k0 * 4);
+            const __amdgpu_buffer_rsrc_t rb_ = rsrc_at(b_org + k0 * g.ldb * 4);
+#pragma unroll
+            for (int v = 0; v < A_RUNS; ++v)
+#pragma unroll
+                for (int e4 = 0; e4 < RUN / 4; ++e4) {
+                    const f32x4 q = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_, a_off[v] + 16 * e4, 0, 0));
+                    ra[s][v][4 * e4 + 0] = q.x;
+                    ra[s][v][4 * e4 + 1] = q.y;
+                    ra[s][v][4 * e4 + 2] = q.z;
+                    ra[s][v][4 * e4 + 3] = q.w;
+                }
+#pragma unroll
+            for (int v = 0; v < B_RUNS; ++v)
+#pragma unroll
+                for (int e = 0; e < RUN; ++e)
+                    rb[s][v][e] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(rb_, b_off[v],
+                                                                    (int)(e * g.ldb * 4), 0));
+            return;
+        }
 #pragma unroll
         for (int v = 0; v < A_RUNS; ++v) {
-            const float *p = a_src[v] + k0;
+            const float *p =
+                (NARROW ? (const float *)(a_org + a_off[v]) : a_src[v]) + k0;
             if constexpr (FULL) {
 #pragma unroll
                 for (int e4 = 0; e4 < RUN / 4; ++e4) {
@@ -236,7 +280,8 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void split_kernel(Args g, int t
         }
 #pragma unroll
         for (int v = 0; v < B_RUNS; ++v) {
-            const float *p = b_src[v] + k0 * g.ldb;
+            const float *p =
+                (NARROW ? (const float *)(b_org + b_off[v]) : b_src[v]) + k0 * g.ldb;
             const int64_t kk = k0 + b_k[v];
 #pragma unroll
             for (int e = 0; e < RUN; ++e) {
@@ -422,8 +467,14 @@ hipError_t launch_split_tile(const Problem &p, hipStream_t s) {
     const int64_t tiles_n = (p.N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > INT32_MAX) return hipErrorInvalidValue;
     const Args g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
-    return launch(split_kernel<T>, dim3((unsigned)(tiles_m * tiles_n)), dim3(T::THREADS), 0, s, g,
-                  (int)tiles_m, (int)tiles_n);
+    // largest lane offsets: the last row of A's block plus a window, the last k
+    // row of B's window plus a row of the block
+    const bool narrow = (((int64_t)(T::BM - 1) * p.lda + BK) * 4 < ((int64_t)1 << 31)) &&
+                        (((int64_t)(BK - 1) * p.ldb + T::BN) * 4 < ((int64_t)1 << 31));
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(T::THREADS);
+    if (narrow)
+        return launch(split_kernel<T, true>, grid, block, 0, s, g, (int)tiles_m, (int)tiles_n);
+    return launch(split_kernel<T, false>, grid, block, 0, s, g, (int)tiles_m, (int)tiles_n);
 }
 
 // 256 x 256 blocks of eight waves (two per SIMD) with 128 x 64 of C each; B
