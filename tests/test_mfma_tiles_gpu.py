@@ -71,8 +71,9 @@ def test_tile_k_zero_and_empty(tile):
 
 
 # Row strides so long that some lane of a block lies 2^31 bytes or more from the
-# block's first row or column: the kernels then address with 64-bit per-lane
-# pointers instead of 32-bit offsets from a uniform base.  (layout, M, N, K, lda,
+# block's first row or column: the kernels (matrix-core and split-precision
+# rungs) then address with 64-bit per-lane pointers instead of 32-bit offsets
+# from a uniform base.  (layout, M, N, K, lda,
 # ldb) with the stored arrays' row counts: A is M x lda (K x lda transposed), B is
 # K x ldb (N x ldb transposed).  Only the logical columns are copied to the GPU.
 WIDE = [
@@ -103,14 +104,20 @@ def test_wide_row_strides(case):
         dev[name] = buf
     stream = torch.cuda.current_stream()
     try:
-        for tile in (0, None):
+        # tile 0 forced, the automatic tile, and (untransposed only) the split rung
+        runs = [0, None] + (["bf16x6"] if (ta, tb) == (0, 0) else [])
+        for tile in runs:
             C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
             log(f"[gpu] wide strides {'T' if ta else 'N'}{'T' if tb else 'N'} tile={tile} "
                 f"M={M} N={N} K={K} lda={lda} ldb={ldb}")
             args = (ta, tb, M, N, K, 1.0, dev["A"].data_ptr(), lda, dev["B"].data_ptr(), ldb, 0.0,
                     C.data_ptr(), N, stream.cuda_stream)
-            st = (sg.sgemm_f32_ex_mfma_tile(*args, tile) if tile is not None
-                  else sg.sgemm_f32_ex_algo(*args, sg.ALGO_MFMA))
+            if tile == "bf16x6":
+                st = sg.sgemm_f32_ex_algo(*args, sg.ALGO_BF16X6)
+            elif tile is not None:
+                st = sg.sgemm_f32_ex_mfma_tile(*args, tile)
+            else:
+                st = sg.sgemm_f32_ex_algo(*args, sg.ALGO_MFMA)
             assert st == 0
             stream.synchronize()
             assert np.array_equal(C.cpu().numpy().astype(np.float64), exact), f"tile {tile}"
