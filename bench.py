@@ -477,7 +477,7 @@ def main(argv=None):
     kavg = sum(kms) / len(kms)
     achieved = flops / (kavg * 1e-3) / 1e12
     rec = {
-        "metric": "SGEMM TFLOP/s (2MNK/t) + % FP32 peak",
+        "metric": "SGEMM TFLOP/s (2MNK/t) + % FP32 peak at 2048\u00d74096\u00d73072 and 8192\u00b3",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
