@@ -34,7 +34,8 @@ OP_T = 1
 EXPORTED = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name",
             "sgemm_f32_ex", "sgemm_f32_ex_algo", "sgemm_f32_colmajor",
             "sgemm_f32_mfma_tiles", "sgemm_f32_mfma_tile_name", "sgemm_f32_mfma_select",
-            "sgemm_f32_mfma_tile", "sgemm_f32_ex_mfma_tile", "sgemm_f32_auto_plan")
+            "sgemm_f32_mfma_tile", "sgemm_f32_ex_mfma_tile", "sgemm_f32_auto_plan",
+            "sgemm_f32_workspace_size", "sgemm_f32_ex_ws")
 
 _lib = None
 
@@ -88,6 +89,11 @@ def lib() -> ctypes.CDLL:
         l.sgemm_f32_ex_algo.restype = i
         l.sgemm_f32_ex_mfma_tile.argtypes = ex_args + [i]
         l.sgemm_f32_ex_mfma_tile.restype = i
+        l.sgemm_f32_workspace_size.argtypes = [i, i, i, i, i]
+        l.sgemm_f32_workspace_size.restype = ctypes.c_size_t
+        l.sgemm_f32_ex_ws.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp, ctypes.c_size_t,
+                                      vp]
+        l.sgemm_f32_ex_ws.restype = i
         ip = ctypes.POINTER(i)
         l.sgemm_f32_auto_plan.argtypes = [i, i, i, i, i, i, ip, ip]
         l.sgemm_f32_auto_plan.restype = i
@@ -138,6 +144,18 @@ def sgemm_f32_auto_plan(transa, transb, M, N, K, compute_units=256):
     algo = lib().sgemm_f32_auto_plan(transa, transb, M, N, K, compute_units,
                                      ctypes.byref(m), ctypes.byref(n))
     return algo, m.value, n.value
+
+
+def sgemm_f32_workspace_size(transa, transb, M, N, K) -> int:
+    """Bytes of workspace sgemm_f32_ex_ws would use (0: no split); no GPU work."""
+    return lib().sgemm_f32_workspace_size(transa, transb, M, N, K)
+
+
+def sgemm_f32_ex_ws(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                    workspace_bytes, stream=0) -> int:
+    """sgemm_f32_ex with a device workspace (split-k when it pays); returns the hipError_t."""
+    return lib().sgemm_f32_ex_ws(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                 workspace, workspace_bytes, stream)
 
 
 def sgemm_f32_mfma_tile(M, N, K, A, lda, B, ldb, C, ldc, stream=0, tile=0) -> int:

@@ -58,20 +58,26 @@ int compute_units() {
     return cus;
 }
 
+// Modelled time of configuration i with the k windows split into `slices`
+// slices: the grid holds tiles * slices work-groups, each over K / slices.
+static double tile_us(int i, int M, int N, int K, int cus, int slices) {
+    const TileChoice &c = kTiles[i];
+    const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * slices;
+    const double per_cu = std::ceil(tiles / cus);
+    const double operands = 4.0 * ((double)M * K + (double)K * N);
+    const double per_cu_tflops =
+        (operands <= 200e6 ? c.tflops_cached : c.tflops_large) / 256.0;  // fitted on 256 CUs
+    const double k_slice = std::ceil((double)K / slices);
+    return per_cu * (2.0 * c.bm * c.bn * k_slice / (per_cu_tflops * 1e6) + c.t1_us) + c.t0_us;
+}
+
 // Index into kTiles of the configuration the model prefers for this shape, and
 // its modelled time in microseconds.
 static int choose_tile(int M, int N, int K, int cus, double *model_us = nullptr) {
     int best = 0;
     double best_us = 0;
     for (int i = 0; i < kTileCount; ++i) {
-        const TileChoice &c = kTiles[i];
-        const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-        const double per_cu = std::ceil(tiles / cus);
-        const double operands = 4.0 * ((double)M * K + (double)K * N);
-        const double per_cu_tflops =
-            (operands <= 200e6 ? c.tflops_cached : c.tflops_large) / 256.0;  // fitted on 256 CUs
-        const double us =
-            per_cu * (2.0 * c.bm * c.bn * (double)K / (per_cu_tflops * 1e6) + c.t1_us) + c.t0_us;
+        const double us = tile_us(i, M, N, K, cus, 1);
         if (i == 0 || us < best_us) {
             best = i;
             best_us = us;
@@ -102,6 +108,31 @@ double mfma_model_us(int M, int N, int K, int cus) {
     double us = 0;
     choose_tile(M, N, K, cus > 0 ? cus : 256, &us);
     return us;
+}
+
+int mfma_tile_bk(int tile) {
+    switch (tile) {
+    case 0: return TileHuge::BK;
+    case 1: return TileWide::BK;
+    case 2: return TileSplit192::BK;
+    case 3: return TileTall::BK;
+    case 4: return TileSmall::BK;
+    case 5: return TileSplit64::BK;
+    case 6: return TileTiny::BK;
+    default: return 0;
+    }
+}
+
+double mfma_model_tile_us(int tile, int M, int N, int K, int cus, int slices) {
+    if (tile < 0 || tile >= kTileCount || slices < 1) return 1e30;
+    return tile_us(tile, M, N, K, cus > 0 ? cus : 256, slices);
+}
+
+hipError_t launch_mfma_splitk(const Problem &p, hipStream_t s, int tile, int slices, float *ws) {
+    if (p.ta) return p.tb ? launch_mfma_tt_splitk(p, s, tile, slices, ws)
+                          : launch_mfma_tn_splitk(p, s, tile, slices, ws);
+    return p.tb ? launch_mfma_nt_splitk(p, s, tile, slices, ws)
+                : launch_mfma_nn_splitk(p, s, tile, slices, ws);
 }
 
 hipError_t launch_mfma_tile(const Problem &p, hipStream_t s, int tile) {

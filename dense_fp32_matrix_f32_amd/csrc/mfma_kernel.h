@@ -671,6 +671,35 @@ bool narrow_offsets(const Problem &p) {
     return a && b;
 }
 
+// Split-k form: work-group b computes block b % tiles over slice b / tiles of the
+// k windows (slice q of S covers windows [q*W/S, (q+1)*W/S)) and stores its
+// partial block, unscaled, to plane q of the workspace (M x N, row stride N).
+// The planes are added in slice order by splitk_reduce (basic.hip).
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_splitk_kernel(GemmArgs g, int tiles_m,
+                                                                        int tiles_n, int slices,
+                                                                        float *ws) {
+    __shared__ __attribute__((aligned(16))) float lds[C::LDS_FLOATS];
+    const int tiles = tiles_m * tiles_n;
+    const int t = blockIdx.x % tiles, slice = blockIdx.x / tiles;
+    int tm, tn;
+    group_tile(t, tiles_m, tiles_n, C::GROUP_M, &tm, &tn);
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int nwin = (g.K + C::BK - 1) / C::BK;
+    const int wb = (int)((int64_t)slice * nwin / slices);
+    const int we = (int)((int64_t)(slice + 1) * nwin / slices);
+    Acc<C> acc;
+    zero_acc<C>(acc);
+    mma_tile<C>(g, lds, m0, n0, wb, we, acc);
+    if (!kw_reduce<C>(lds, acc)) return;
+    GemmArgs o = g;
+    o.C = ws + (int64_t)slice * g.M * g.N;
+    o.ldc = g.N;
+    o.alpha = 1.0f;
+    o.beta = 0.0f;
+    store_tile<C>(o, m0, n0, acc);
+}
+
 template <class T, bool TA, bool TB>
 hipError_t launch_tile(const Problem &p, hipStream_t s) {
     using C = Cfg<T, TA, TB>;
@@ -684,6 +713,24 @@ hipError_t launch_tile(const Problem &p, hipStream_t s) {
                       (int)tiles_n);
     return launch(mfma_kernel<Cfg<T, TA, TB, false>>, grid, block, 0, s, g, (int)tiles_m,
                   (int)tiles_n);
+}
+
+// The split-k form of configuration T with `slices` slices; the caller has checked
+// that every slice holds at least one k window and that the workspace holds
+// slices * M * N floats.
+template <class T, bool TA, bool TB>
+hipError_t launch_tile_splitk(const Problem &p, hipStream_t s, int slices, float *ws) {
+    using C = Cfg<T, TA, TB>;
+    const int64_t tiles_m = (p.M + C::BM - 1) / C::BM;
+    const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
+    if (tiles_m * tiles_n * slices > INT32_MAX) return hipErrorInvalidValue;
+    const GemmArgs g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
+    const dim3 grid((unsigned)(tiles_m * tiles_n * slices)), block(C::THREADS);
+    if (narrow_offsets<T, TA, TB>(p))
+        return launch(mfma_splitk_kernel<Cfg<T, TA, TB, true>>, grid, block, 0, s, g, (int)tiles_m,
+                      (int)tiles_n, slices, ws);
+    return launch(mfma_splitk_kernel<Cfg<T, TA, TB, false>>, grid, block, 0, s, g, (int)tiles_m,
+                  (int)tiles_n, slices, ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -709,6 +756,12 @@ hipError_t launch_mfma_nn(const Problem &p, hipStream_t s, int tile);
 hipError_t launch_mfma_nt(const Problem &p, hipStream_t s, int tile);
 hipError_t launch_mfma_tn(const Problem &p, hipStream_t s, int tile);
 hipError_t launch_mfma_tt(const Problem &p, hipStream_t s, int tile);
+// Split-k launches of the configurations that split-k uses (TileWide, TileSmall,
+// TileSplit64); hipErrorInvalidValue for the others.
+hipError_t launch_mfma_nn_splitk(const Problem &p, hipStream_t s, int tile, int slices, float *ws);
+hipError_t launch_mfma_nt_splitk(const Problem &p, hipStream_t s, int tile, int slices, float *ws);
+hipError_t launch_mfma_tn_splitk(const Problem &p, hipStream_t s, int tile, int slices, float *ws);
+hipError_t launch_mfma_tt_splitk(const Problem &p, hipStream_t s, int tile, int slices, float *ws);
 
 #define SGEMM_MFMA_LAUNCHER(NAME, TA, TB)                                                     \
     hipError_t NAME(const Problem &p, hipStream_t s, int tile) {                             \
@@ -720,6 +773,14 @@ hipError_t launch_mfma_tt(const Problem &p, hipStream_t s, int tile);
         case 4: return launch_tile<TileSmall, TA, TB>(p, s);                                  \
         case 5: return launch_tile<TileSplit64, TA, TB>(p, s);                                \
         case 6: return launch_tile<TileTiny, TA, TB>(p, s);                                   \
+        default: return hipErrorInvalidValue;                                                 \
+        }                                                                                     \
+    }                                                                                         \
+    hipError_t NAME##_splitk(const Problem &p, hipStream_t s, int tile, int slices, float *ws) { \
+        switch (tile) {                                                                       \
+        case 1: return launch_tile_splitk<TileWide, TA, TB>(p, s, slices, ws);                \
+        case 4: return launch_tile_splitk<TileSmall, TA, TB>(p, s, slices, ws);               \
+        case 5: return launch_tile_splitk<TileSplit64, TA, TB>(p, s, slices, ws);             \
         default: return hipErrorInvalidValue;                                                 \
         }                                                                                     \
     }

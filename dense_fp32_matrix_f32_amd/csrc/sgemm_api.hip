@@ -148,6 +148,51 @@ hipError_t launch_auto_mfma(const Problem &p, hipStream_t s) {
     return e;
 }
 
+// ---------------------------------------------------------------------------
+// Split-k with a caller-provided workspace.  Products with few blocks of C and a
+// long k leave most CUs idle (128 x 128 x 65536: 4 blocks of 64 x 64); they split
+// k into slices whose unscaled partial products go to workspace planes, added in
+// slice order by a second kernel (deterministic, no atomics).  The few-rows
+// kernel was tried the same way (512-byte row segments, 16 slices for 1 x 4096 x
+// 4096) and lost to the plain kernel by the second launch, so it never splits.
+enum WsKind { WS_NONE = 0, WS_MFMA = 1 };
+struct WsPlan {
+    int kind, tile, slices;
+};
+
+constexpr double kReduceBytesPerUs = 2.5e6;
+constexpr double kReduceLaunchUs = 3.0;
+
+double reduce_us(const Problem &p, int slices) {
+    const double plane = 4.0 * p.M * (double)p.N;
+    return kReduceLaunchUs + (slices * plane + plane * (p.beta != 0.0f ? 2 : 1)) / kReduceBytesPerUs;
+}
+
+int64_t ws_bytes(const WsPlan &w, const Problem &p) {
+    return w.kind == WS_NONE ? 0 : (int64_t)w.slices * p.M * p.N * (int64_t)sizeof(float);
+}
+
+WsPlan plan_workspace(const Problem &p, int algo, int cus) {
+    WsPlan none{WS_NONE, 0, 1};
+    if (p.M == 0 || p.N == 0 || p.K == 0 || algo != SGEMM_F32_ALGO_MFMA) return none;
+    const double whole = sgemm::mfma_model_us(p.M, p.N, p.K, cus);
+    WsPlan best = none;
+    double best_us = whole;
+    static constexpr int kSplitTiles[] = {1, 4, 5};
+    for (int tile : kSplitTiles) {
+        const int64_t nwin = ((int64_t)p.K + sgemm::mfma_tile_bk(tile) - 1) / sgemm::mfma_tile_bk(tile);
+        for (int slices = 2; slices <= 128 && 2 * (int64_t)slices <= nwin; slices *= 2) {
+            const double us = sgemm::mfma_model_tile_us(tile, p.M, p.N, p.K, cus, slices) +
+                              reduce_us(p, slices);
+            if (us < best_us) {
+                best_us = us;
+                best = WsPlan{WS_MFMA, tile, slices};
+            }
+        }
+    }
+    return best_us < 0.8 * whole ? best : none;
+}
+
 bool handles_transposes(int algo) {
     return algo == SGEMM_F32_ALGO_AUTO || algo == SGEMM_F32_ALGO_NAIVE ||
            algo == SGEMM_F32_ALGO_LDS_TILED || algo == SGEMM_F32_ALGO_MFMA;
@@ -247,6 +292,44 @@ extern "C" hipError_t sgemm_f32_ex_algo(int transa, int transb, int M, int N, in
     case SGEMM_F32_ALGO_BF16X6: return sgemm::launch_split(p, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+extern "C" size_t sgemm_f32_workspace_size(int transa, int transb, int M, int N, int K) {
+    if ((transa != SGEMM_F32_OP_N && transa != SGEMM_F32_OP_T) ||
+        (transb != SGEMM_F32_OP_N && transb != SGEMM_F32_OP_T) || M < 0 || N < 0 || K < 0)
+        return 0;
+    Problem p{M, N, K, nullptr, 1, nullptr, 1, nullptr, 1};
+    p.ta = transa == SGEMM_F32_OP_T;
+    p.tb = transb == SGEMM_F32_OP_T;
+    const WsPlan w = plan_workspace(p, choose(transa, transb, M, N, K), sgemm::compute_units());
+    return (size_t)ws_bytes(w, p);
+}
+
+extern "C" hipError_t sgemm_f32_ex_ws(int transa, int transb, int M, int N, int K, float alpha,
+                                      const float *A, int lda, const float *B, int ldb,
+                                      float beta, float *C, int ldc, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    hipError_t st;
+    if (trivial(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, &st))
+        return st;
+    if (workspace != nullptr && workspace_bytes > 0 && ((uintptr_t)workspace & 15) != 0)
+        return hipErrorInvalidValue;
+    const Problem p = problem(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    const int algo = choose(transa, transb, M, N, K);
+    const WsPlan w = plan_workspace(p, algo, sgemm::compute_units());
+    const int64_t need = ws_bytes(w, p);
+    if (w.kind == WS_NONE || workspace == nullptr || (uint64_t)need > workspace_bytes)
+        return sgemm_f32_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    // the part of the workspace used must not overlap the operands or C
+    const Extent ws{(uintptr_t)workspace, (uintptr_t)workspace + (uintptr_t)need};
+    const Extent c = extent(C, M, N, ldc);
+    const Extent a = transa ? extent(A, K, M, lda) : extent(A, M, K, lda);
+    const Extent b = transb ? extent(B, N, K, ldb) : extent(B, K, N, ldb);
+    if (overlaps(ws, a) || overlaps(ws, b) || overlaps(ws, c)) return hipErrorInvalidValue;
+    float *planes = (float *)workspace;
+    st = sgemm::launch_mfma_splitk(p, stream, w.tile, w.slices, planes);
+    if (st != hipSuccess) return st;
+    return sgemm::launch_splitk_reduce(p, w.slices, planes, stream);
 }
 
 extern "C" hipError_t sgemm_f32_ex(int transa, int transb, int M, int N, int K, float alpha,

@@ -45,6 +45,7 @@
 #define SGEMM_F32_H
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -203,6 +204,39 @@ hipError_t sgemm_f32_ex_mfma_tile(int transa, int transb, int M, int N, int K, f
                                   const float *B, int ldb, float beta,
                                   float *C, int ldc,
                                   hipStream_t stream, int tile);
+
+/*
+ * Split-k with a caller-provided workspace (the library still allocates
+ * nothing).  Products with few blocks of C and a long k (for example 128 x 128
+ * x 65536) leave most CUs idle on the matrix-core rung.  Given room,
+ * sgemm_f32_ex_ws() splits k into S slices:
+ * the first kernel writes each slice's unscaled partial product to a plane of
+ * the workspace (S planes of M x N floats, row stride N), the second forms
+ *     C = alpha * (plane 0 + plane 1 + ... + plane S-1) + beta * C
+ * adding the planes in slice order, so results are reproducible run to run
+ * (they differ from sgemm_f32_ex() only in summation order, within the same
+ * bound).  The choice of S and of the block configuration comes from the same
+ * cost model as the rest of the automatic choice; the split is taken only when
+ * modelled at least 20% faster.
+ *
+ * sgemm_f32_workspace_size()  bytes sgemm_f32_ex_ws() would use for these
+ *                             arguments on the current device (0: no split;
+ *                             also 0 for invalid arguments).  No GPU work.
+ * sgemm_f32_ex_ws()           the general form of sgemm_f32_ex() with a device
+ *                             workspace of workspace_bytes bytes, 16-byte
+ *                             aligned, owned by the caller and not overlapping
+ *                             A, B or C (hipErrorInvalidValue otherwise).  With
+ *                             workspace == NULL or too few bytes it is exactly
+ *                             sgemm_f32_ex().  Calls that overlap in time must
+ *                             not share a workspace.
+ */
+size_t sgemm_f32_workspace_size(int transa, int transb, int M, int N, int K);
+hipError_t sgemm_f32_ex_ws(int transa, int transb, int M, int N, int K, float alpha,
+                           const float *A, int lda,
+                           const float *B, int ldb, float beta,
+                           float *C, int ldc,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * How SGEMM_F32_ALGO_AUTO runs an M x N x K product with the given storage

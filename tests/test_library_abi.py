@@ -189,6 +189,35 @@ def test_auto_plan_splits_edge_strips():
             assert algo == sg.ALGO_MFMA and min(m, n) >= 56
 
 
+def test_workspace_size_and_validation():
+    # few blocks of C and a long k: split; large products and the streaming rungs: not
+    for shape in [(128, 128, 65536), (64, 64, 4096), (256, 256, 16384), (512, 512, 32768)]:
+        need = sg.sgemm_f32_workspace_size(0, 0, *shape)
+        assert need > 0 and need % (4 * shape[0] * shape[1]) == 0, shape
+    for shape in [(8192, 8192, 8192), (2048, 3072, 4096), (1024, 1024, 1024), (1, 4096, 4096),
+                  (4096, 1, 4096), (1, 100000, 4096), (0, 5, 5), (5, 5, 0)]:
+        assert sg.sgemm_f32_workspace_size(0, 0, *shape) == 0, shape
+    assert sg.sgemm_f32_workspace_size(2, 0, 128, 128, 65536) == 0
+    assert sg.sgemm_f32_workspace_size(0, 0, -1, 128, 65536) == 0
+    M, N, K = 128, 128, 65536
+    need = sg.sgemm_f32_workspace_size(0, 0, M, N, K)
+    a, b, c = 1 << 40, 1 << 41, 1 << 42
+
+    def call(ws, nbytes, **kw):
+        args = dict(A=a, B=b, C=c)
+        args.update(kw)
+        return sg.sgemm_f32_ex_ws(0, 0, M, N, K, 1.0, args["A"], K, args["B"], N, 0.0, args["C"],
+                                  N, ws, nbytes, 0)
+    # a misaligned workspace, and one that overlaps C, A or B, fail before any launch
+    assert call((1 << 43) + 4, need) == INVALID
+    assert call(c + 64, need) == INVALID
+    assert call(a + 4 * M * K - 16, need) == INVALID
+    assert call(b - 16, need) == INVALID
+    # the usual argument checks come first
+    assert sg.sgemm_f32_ex_ws(0, 0, M, N, K, 1.0, a, K - 1, b, N, 0.0, c, N, 1 << 43, need, 0) \
+        == INVALID
+
+
 def test_mfma_tile_entry_validates():
     n = sg.sgemm_f32_mfma_tiles()
     for tile in (-1, n):

@@ -4,8 +4,8 @@ The library allocates nothing and never synchronizes, so a sequence of calls can
 be captured into a graph and replayed.  The captured sequence covers every
 kernel family the automatic choice launches: blocks of the matrix cores, a
 product split into blocks and an edge strip (two launches), the few-rows and
-few-columns streaming kernels, C = beta*C for K = 0, and accumulation into C
-(beta = 1).  The graph is replayed several times with eager work and
+few-columns streaming kernels, C = beta*C for K = 0, accumulation into C
+(beta = 1), and split-k through a workspace.  The graph is replayed several times with eager work and
 synchronizations in between (the operands change between replays); every replay
 is compared with the oracle, bitwise on small-integer data.  A second test runs
 products on two streams at once.
@@ -20,9 +20,9 @@ from gpu_helpers import log, sample_indices, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
-# (M, N, K, beta)
+# (M, N, K, beta); the last one runs split-k through a workspace
 CAPTURED = [(1000, 1100, 700, 0.0), (2049, 4097, 1023, 0.0), (1, 2049, 515, 0.0),
-            (3000, 3, 700, 0.0), (100, 100, 0, 0.0), (300, 200, 150, 1.0)]
+            (3000, 3, 700, 0.0), (100, 100, 0, 0.0), (300, 200, 150, 1.0), (128, 96, 20000, 1.0)]
 
 
 def _exact(A, B, beta, C0, rows=None, cols=None):
@@ -56,14 +56,22 @@ def test_graph_capture_and_replay():
         cases.append(dict(M=M, N=N, K=K, beta=beta, A=A, B=B, C0=C0, dA=dA, dB=dB, dC=dC))
     torch.cuda.synchronize()
 
+    last = cases[-1]
+    need = sg.sgemm_f32_workspace_size(0, 0, last["M"], last["N"], last["K"])
+    assert need > 0
+    ws = torch.empty(need // 4, dtype=torch.float32, device="cuda")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         s = torch.cuda.current_stream().cuda_stream
-        for c in cases:
+        for c in cases[:-1]:
             st = sg.sgemm_f32_ex(0, 0, c["M"], c["N"], c["K"], 1.0, c["dA"].data_ptr(),
                                  max(c["K"], 1), c["dB"].data_ptr(), c["N"], c["beta"],
                                  c["dC"].data_ptr(), c["N"], s)
             assert st == 0
+        st = sg.sgemm_f32_ex_ws(0, 0, last["M"], last["N"], last["K"], 1.0, last["dA"].data_ptr(),
+                                last["K"], last["dB"].data_ptr(), last["N"], last["beta"],
+                                last["dC"].data_ptr(), last["N"], ws.data_ptr(), need, s)
+        assert st == 0
     # capture records the launches without running them
     for replay in range(3):
         log(f"[gpu] graph replay {replay}")
