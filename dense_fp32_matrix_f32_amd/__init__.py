@@ -41,15 +41,17 @@ def _operand(t, name):
     raise ValueError(f"{name} needs a unit stride in one dimension")
 
 
-def matmul(A, B, out=None, algo="auto", stream=None, alpha=1.0, beta=0.0):
+def matmul(A, B, out=None, algo="auto", stream=None, alpha=1.0, beta=0.0, workspace=None):
     """Return C = alpha * A @ B + beta * out for 2-D float32 CUDA tensors.
 
     Row-major tensors and views with a row stride are passed as they are;
     transposed views (``X.t()``) are passed as transposed operands, without a
     copy.  ``out`` must be row-major; it is read only when beta != 0 (a new
-    tensor is allocated when it is None, which needs beta == 0).  The product is
-    enqueued on ``stream`` (default: torch's current stream) without
-    synchronising."""
+    tensor is allocated when it is None, which needs beta == 0).  With algo
+    "auto", ``workspace`` (a contiguous CUDA tensor, or "auto" to allocate the
+    size sgemm_f32_workspace_size asks for through torch) lets products with few
+    blocks of C split k across work-groups.  The product is enqueued on
+    ``stream`` (default: torch's current stream) without synchronising."""
     import torch
     pa, lda, ta = _operand(A, "A")
     pb, ldb, tb = _operand(B, "B")
@@ -69,8 +71,20 @@ def matmul(A, B, out=None, algo="auto", stream=None, alpha=1.0, beta=0.0):
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     algo_id = ALGOS[algo] if isinstance(algo, str) else int(algo)
     with torch.cuda.device(A.device):
-        st = sgemm_f32_ex_algo(int(ta), int(tb), M, N, K, float(alpha), pa, lda, pb, ldb,
-                               float(beta), pc, ldc, s.cuda_stream, algo_id)
+        if workspace is not None and algo_id == ALGO_AUTO:
+            if isinstance(workspace, str):
+                if workspace != "auto":
+                    raise ValueError('workspace must be a tensor, "auto" or None')
+                nbytes = sgemm_f32_workspace_size(int(ta), int(tb), M, N, K)
+                workspace = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=A.device)
+            if not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous CUDA tensor")
+            st = sgemm_f32_ex_ws(int(ta), int(tb), M, N, K, float(alpha), pa, lda, pb, ldb,
+                                 float(beta), pc, ldc, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), s.cuda_stream)
+        else:
+            st = sgemm_f32_ex_algo(int(ta), int(tb), M, N, K, float(alpha), pa, lda, pb, ldb,
+                                   float(beta), pc, ldc, s.cuda_stream, algo_id)
     if st != 0:
         raise SgemmError(st)
     return out

@@ -78,3 +78,16 @@ def test_small_workspace_is_plain_ex(case):
                            K if tb else N, 0.0, dC.data_ptr(), N, s.cuda_stream) == 0
     s.synchronize()
     assert np.array_equal(C_small.view(np.uint32), dC.cpu().numpy().view(np.uint32))
+
+
+def test_matmul_helper_workspace():
+    torch = torch_cuda()
+    M, N, K = 128, 96, 30000
+    A = synthgen.matrix(M, K, seed=44, stream=0, dist="smallint")
+    B = synthgen.matrix(K, N, seed=44, stream=1, dist="smallint")
+    At, Bt = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    want, _ = oracle.sgemm(A, B)
+    for ws in ("auto", torch.empty(sg.sgemm_f32_workspace_size(0, 0, M, N, K) // 4, device="cuda")):
+        C = sg.matmul(At, Bt, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), want)
