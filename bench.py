@@ -113,15 +113,21 @@ def make_inputs(torch, M, N, K, seed, dist="normal", layout=(0, 0)):
     return A, B, dA, dB, dC
 
 
-def time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warmup, layout=(0, 0)):
+def time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warmup, layout=(0, 0),
+                 workspace=None):
     """Warm-up, then `steps` timed launches: wall clock between two full
-    synchronisations, and per-launch HIP events on the launch stream."""
+    synchronisations, and per-launch HIP events on the launch stream.  With a
+    workspace tensor, the product goes through sgemm_f32_ex_ws."""
     stream = torch.cuda.current_stream()
     ta, tb = layout
     lda, ldb, ldc = (M if ta else K), (K if tb else N), N
 
     def call():
-        if layout == (0, 0):
+        if workspace is not None:
+            st = sg.sgemm_f32_ex_ws(ta, tb, M, N, K, 1.0, dA.data_ptr(), lda, dB.data_ptr(), ldb,
+                                    0.0, dC.data_ptr(), ldc, workspace.data_ptr(),
+                                    4 * workspace.numel(), stream.cuda_stream)
+        elif layout == (0, 0):
             st = sg.sgemm_f32_algo(M, N, K, dA.data_ptr(), lda, dB.data_ptr(), ldb,
                                    dC.data_ptr(), ldc, stream.cuda_stream, algo)
         else:
@@ -417,6 +423,9 @@ def main(argv=None):
     p.add_argument("--configs", action="store_true",
                    help="report every workload (512^3, 1024^3, 2048x3072x4096, 4095x4097x1023, "
                         "1x4096x4096, 8192^3) instead, one JSON line each")
+    p.add_argument("--workspace", action="store_true",
+                   help="time sgemm_f32_ex_ws with the workspace sgemm_f32_workspace_size asks "
+                        "for (split-k for products with few blocks of C)")
     p.add_argument("--tiles", action="store_true",
                    help="time every tile configuration of the matrix-core rung on --shape, or on "
                         "the tile-model shapes with --shape all (one JSON line per configuration)")
@@ -468,9 +477,14 @@ def main(argv=None):
     used = chosen if algo == sg.ALGO_AUTO else algo
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up, algo "
           f"{sg.sgemm_f32_algo_name(used)}", file=sys.stderr, flush=True)
+    ws = None
+    if args.workspace:
+        nbytes = sg.sgemm_f32_workspace_size(layout[0], layout[1], M, N, K)
+        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device="cuda")
+        print(f"[bench] workspace {nbytes} bytes (sgemm_f32_ex_ws)", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall, kms = time_product(torch, sg, M, N, K, dA, dB, dC, algo, args.steps, args.warmup,
-                             layout)
+                             layout, workspace=ws)
     flops = algorithmic_flops(M, N, K)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (wall / args.steps) / 1e12
@@ -492,7 +506,9 @@ def main(argv=None):
         "pct_fp32_peak": round(100 * value / PEAK_FP32_TFLOPS, 2),
         "config": {"workload": f"C=A*B fp32 row-major M={M} N={N} K={K}, A,B iid N(0,1) "
                                f"seed {args.seed}" +
-                               ("" if layout == (0, 0) else f", operands {args.layout}"),
+                               ("" if layout == (0, 0) else f", operands {args.layout}") +
+                               (f", split-k workspace {4 * ws.numel()} bytes" if ws is not None
+                                else ""),
                    "M": M, "N": N, "K": K, "algo": sg.sgemm_f32_algo_name(used),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,

@@ -10,7 +10,6 @@
 
 namespace sgemm {
 
-typedef float f32x4_basic __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // No product (K == 0, the empty sum, or alpha == 0): C = beta*C, and C = 0
@@ -37,48 +36,40 @@ hipError_t launch_scale(const Problem &p, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Split-k: C = alpha * (plane 0 + plane 1 + ... + plane S-1) + beta * C, the
 // planes (M x N, row stride N) added in slice order, so the result does not
-// depend on which work-group finished first.  Four adjacent elements of a row
-// per work-item when N is a multiple of 4.
-template <bool VEC>
+// depend on which work-group finished first.  One element per work-item; the
+// loads of 16 planes are issued before they are added, so a work-item keeps 16
+// reads in flight instead of waiting for each plane in turn.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(int M, int N, int S,
                                                             const float *__restrict__ ws,
                                                             float *__restrict__ C, int64_t ldc,
                                                             float alpha, float beta) {
-    constexpr int W = VEC ? 4 : 1;
+    constexpr int U = 16;
     const int64_t plane = (int64_t)M * N;
-    const int64_t total = plane / W;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-        const int64_t flat = e * W;
-        const int64_t i = flat / N, j = flat - i * N;
-        float sum[W];
-        if constexpr (VEC) {
-            f32x4_basic v = *(const f32x4_basic *)(ws + flat);
-            sum[0] = v.x, sum[1] = v.y, sum[2] = v.z, sum[3] = v.w;
-            for (int q = 1; q < S; ++q) {
-                v = *(const f32x4_basic *)(ws + q * plane + flat);
-                sum[0] += v.x, sum[1] += v.y, sum[2] += v.z, sum[3] += v.w;
-            }
-        } else {
-            sum[0] = ws[flat];
-            for (int q = 1; q < S; ++q) sum[0] += ws[q * plane + flat];
-        }
-        float *c = C + i * ldc + j;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < plane; e += stride) {
+        const float *src = ws + e;
+        float sum = 0.0f;
+        int q = 0;
+        for (; q + U <= S; q += U) {
+            float v[U];
 #pragma unroll
-        for (int w = 0; w < W; ++w) c[w] = epilogue(sum[w], alpha, beta, c + w);
+            for (int u = 0; u < U; ++u) v[u] = src[(q + u) * plane];
+#pragma unroll
+            for (int u = 0; u < U; ++u) sum += v[u];
+        }
+        for (; q < S; ++q) sum += src[q * plane];
+        const int64_t i = e / N, j = e - i * N;
+        float *c = C + i * ldc + j;
+        *c = epilogue(sum, alpha, beta, c);
     }
 }
 
 hipError_t launch_splitk_reduce(const Problem &p, int slices, const float *ws, hipStream_t s) {
-    const bool vec = p.N % 4 == 0;
-    const int64_t items = (int64_t)p.M * p.N / (vec ? 4 : 1);
+    const int64_t items = (int64_t)p.M * p.N;
     int64_t blocks = (items + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    if (vec)
-        return launch(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, p.M,
-                      p.N, slices, ws, p.C, p.ldc, p.alpha, p.beta);
-    return launch(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, p.M, p.N,
-                  slices, ws, p.C, p.ldc, p.alpha, p.beta);
+    if (blocks > 16384) blocks = 16384;
+    return launch(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.M, p.N, slices,
+                  ws, p.C, p.ldc, p.alpha, p.beta);
 }
 
 // Element strides of op(A) (rows i, k) and op(B) (k, columns j).
