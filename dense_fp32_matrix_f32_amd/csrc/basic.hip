@@ -34,42 +34,92 @@ hipError_t launch_scale(const Problem &p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-k: C = alpha * (plane 0 + plane 1 + ... + plane S-1) + beta * C, the
-// planes (M x N, row stride N) added in slice order, so the result does not
-// depend on which work-group finished first.  One element per work-item; the
-// loads of 16 planes are issued before they are added, so a work-item keeps 16
-// reads in flight instead of waiting for each plane in turn.
+// Split-k: C = alpha * (sum of the S planes) + beta * C, the planes (M x N, row
+// stride N) added in an order fixed by (M, N, S) alone, so the result does not
+// depend on which work-group finished first.  A work-group covers E = 256/G
+// consecutive elements with G groups of work-items: group g adds planes
+// [g*S/G, (g+1)*S/G) in order, then group 0 adds the G partial sums in order.
+// G > 1 spreads small outputs (128 x 128 is 64 work-groups of 256 elements)
+// over more CUs and shortens each work-item's chain of plane loads.  Loads are
+// issued in batches of 16 (then 4) before they are added, so several reads are
+// in flight per work-item.
+template <int G>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(int M, int N, int S,
                                                             const float *__restrict__ ws,
                                                             float *__restrict__ C, int64_t ldc,
                                                             float alpha, float beta) {
-    constexpr int U = 16;
+    constexpr int E = 256 / G;
+    __shared__ float part[G][E];
+    const int el = threadIdx.x % E, g = threadIdx.x / E;
+    const int q0 = (int)((int64_t)g * S / G), q1 = (int)((int64_t)(g + 1) * S / G);
     const int64_t plane = (int64_t)M * N;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < plane; e += stride) {
-        const float *src = ws + e;
+    // The loop bound depends on the work-group only, so every work-item reaches
+    // each barrier.
+    for (int64_t base = (int64_t)blockIdx.x * E; base < plane; base += (int64_t)gridDim.x * E) {
+        const int64_t e = base + el;
         float sum = 0.0f;
-        int q = 0;
-        for (; q + U <= S; q += U) {
-            float v[U];
+        if (e < plane) {
+            const float *src = ws + e;
+            int q = q0;
+            for (; q + 16 <= q1; q += 16) {
+                float v[16];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = src[(q + u) * plane];
+                for (int u = 0; u < 16; ++u) v[u] = src[(q + u) * plane];
 #pragma unroll
-            for (int u = 0; u < U; ++u) sum += v[u];
+                for (int u = 0; u < 16; ++u) sum += v[u];
+            }
+            for (; q + 4 <= q1; q += 4) {
+                float v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = src[(q + u) * plane];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sum += v[u];
+            }
+            for (; q < q1; ++q) sum += src[q * plane];
         }
-        for (; q < S; ++q) sum += src[q * plane];
-        const int64_t i = e / N, j = e - i * N;
-        float *c = C + i * ldc + j;
-        *c = epilogue(sum, alpha, beta, c);
+        if constexpr (G > 1) {
+            part[g][el] = sum;
+            __syncthreads();
+            if (g == 0) {
+#pragma unroll
+                for (int h = 1; h < G; ++h) sum += part[h][el];
+            }
+            __syncthreads();
+        }
+        if (g == 0 && e < plane) {
+            const int64_t i = e / N, j = e - i * N;
+            float *c = C + i * ldc + j;
+            *c = epilogue(sum, alpha, beta, c);
+        }
     }
 }
 
-hipError_t launch_splitk_reduce(const Problem &p, int slices, const float *ws, hipStream_t s) {
+// Plane groups per output element: the fewest (up to 16, at most S) that give
+// 2048 work-groups, eight per CU.
+static int splitk_reduce_groups(int64_t items, int slices) {
+    int g = 1;
+    while (g < 16 && 2 * g <= slices && (items * g + 255) / 256 < 2048) g *= 2;
+    return g;
+}
+
+template <int G>
+static hipError_t launch_reduce_g(const Problem &p, int slices, const float *ws, hipStream_t s) {
+    constexpr int E = 256 / G;
     const int64_t items = (int64_t)p.M * p.N;
-    int64_t blocks = (items + 255) / 256;
+    int64_t blocks = (items + E - 1) / E;
     if (blocks > 16384) blocks = 16384;
-    return launch(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.M, p.N, slices,
-                  ws, p.C, p.ldc, p.alpha, p.beta);
+    return launch(splitk_reduce_kernel<G>, dim3((unsigned)blocks), dim3(256), 0, s, p.M, p.N,
+                  slices, ws, p.C, p.ldc, p.alpha, p.beta);
+}
+
+hipError_t launch_splitk_reduce(const Problem &p, int slices, const float *ws, hipStream_t s) {
+    switch (splitk_reduce_groups((int64_t)p.M * p.N, slices)) {
+        case 1: return launch_reduce_g<1>(p, slices, ws, s);
+        case 2: return launch_reduce_g<2>(p, slices, ws, s);
+        case 4: return launch_reduce_g<4>(p, slices, ws, s);
+        case 8: return launch_reduce_g<8>(p, slices, ws, s);
+        default: return launch_reduce_g<16>(p, slices, ws, s);
+    }
 }
 
 // Element strides of op(A) (rows i, k) and op(B) (k, columns j).

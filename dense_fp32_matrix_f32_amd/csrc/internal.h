@@ -65,12 +65,14 @@ hipError_t launch_split(const Problem &p, hipStream_t s);
 hipError_t launch_skinny(const Problem &p, hipStream_t s);
 // Split-k: `slices` unscaled partial products of op(A)*op(B) go to the workspace
 // planes ws[q*M*N + i*N + j], then launch_splitk_reduce() forms
-// C = alpha * (sum over q in order) + beta * C.  launch_mfma_splitk() takes the
+// C = alpha * (sum over q) + beta * C, adding the planes in an order fixed by
+// (M, N, slices).  launch_mfma_splitk() takes the
 // configurations TileWide (1), TileSmall (4) and TileSplit64 (5).
 hipError_t launch_mfma_splitk(const Problem &p, hipStream_t s, int tile, int slices, float *ws);
 hipError_t launch_splitk_reduce(const Problem &p, int slices, const float *ws, hipStream_t s);
-// Modelled time (microseconds) of configuration `tile` on `cus` CUs when the k
-// windows are split into `slices` slices (1: no split), products only.
+// Modelled time (microseconds) of the product kernel of configuration `tile` on
+// `cus` CUs when the k windows are split into `slices` slices (products only,
+// not the reduction).
 double mfma_model_tile_us(int tile, int M, int N, int K, int cus, int slices);
 // k window of configuration `tile` (0 for an unknown id).
 int mfma_tile_bk(int tile);

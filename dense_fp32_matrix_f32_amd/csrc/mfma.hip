@@ -58,17 +58,50 @@ int compute_units() {
     return cus;
 }
 
-// Modelled time of configuration i with the k windows split into `slices`
-// slices: the grid holds tiles * slices work-groups, each over K / slices.
-static double tile_us(int i, int M, int N, int K, int cus, int slices) {
+// A work-group cannot go faster than its chain of k windows allows: each window
+// waits for loads that were issued a fixed number of windows earlier.  With one
+// work-group per CU nothing else hides that wait, and configurations with little
+// arithmetic per window (32 x 32 blocks) run at about half their throughput on
+// long k.  Measured per window: about 0.18 us while A and B fit in 8 MiB (the
+// L2 caches), 0.34 us for larger operands.
+static double window_floor_us(double operand_bytes) {
+    return operand_bytes <= 8.0 * 1024 * 1024 ? 0.18 : 0.34;
+}
+
+static double per_cu_rate(const TileChoice &c, double operand_bytes) {
+    return (operand_bytes <= 200e6 ? c.tflops_cached : c.tflops_large) / 256.0;  // fitted on 256 CUs
+}
+
+// Modelled time of configuration i on the whole k range.
+static double tile_us(int i, int M, int N, int K, int cus) {
+    const TileChoice &c = kTiles[i];
+    const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const double per_cu = std::ceil(tiles / cus);
+    const double operands = 4.0 * ((double)M * K + (double)K * N);
+    double work = 2.0 * c.bm * c.bn * (double)K / (per_cu_rate(c, operands) * 1e6);
+    if (per_cu == 1) {
+        const double windows = std::ceil((double)K / mfma_tile_bk(i));
+        work = std::fmax(work, windows * window_floor_us(operands));
+    }
+    return per_cu * (work + c.t1_us) + c.t0_us;
+}
+
+// Modelled time of the product kernel of configuration i with the k windows
+// split into `slices` slices (tiles * slices work-groups over K / slices each).
+// Fitted separately on split launches (20 shapes, 3 configurations, 2..128
+// slices): work-groups of short k overlap their prologue and epilogue with the
+// other work-group resident on the CU, so t1 is paid once, not per round, and
+// the window floor applies to every second round.
+static double split_tile_us(int i, int M, int N, int K, int cus, int slices) {
     const TileChoice &c = kTiles[i];
     const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * slices;
     const double per_cu = std::ceil(tiles / cus);
     const double operands = 4.0 * ((double)M * K + (double)K * N);
-    const double per_cu_tflops =
-        (operands <= 200e6 ? c.tflops_cached : c.tflops_large) / 256.0;  // fitted on 256 CUs
     const double k_slice = std::ceil((double)K / slices);
-    return per_cu * (2.0 * c.bm * c.bn * k_slice / (per_cu_tflops * 1e6) + c.t1_us) + c.t0_us;
+    const double work = per_cu * 2.0 * c.bm * c.bn * k_slice / (per_cu_rate(c, operands) * 1e6);
+    const double floor = std::ceil(per_cu / 2) * std::ceil(k_slice / mfma_tile_bk(i)) *
+                         window_floor_us(operands);
+    return std::fmax(work, floor) + c.t1_us + c.t0_us;
 }
 
 // Index into kTiles of the configuration the model prefers for this shape, and
@@ -77,7 +110,7 @@ static int choose_tile(int M, int N, int K, int cus, double *model_us = nullptr)
     int best = 0;
     double best_us = 0;
     for (int i = 0; i < kTileCount; ++i) {
-        const double us = tile_us(i, M, N, K, cus, 1);
+        const double us = tile_us(i, M, N, K, cus);
         if (i == 0 || us < best_us) {
             best = i;
             best_us = us;
@@ -125,7 +158,7 @@ int mfma_tile_bk(int tile) {
 
 double mfma_model_tile_us(int tile, int M, int N, int K, int cus, int slices) {
     if (tile < 0 || tile >= kTileCount || slices < 1) return 1e30;
-    return tile_us(tile, M, N, K, cus > 0 ? cus : 256, slices);
+    return split_tile_us(tile, M, N, K, cus > 0 ? cus : 256, slices);
 }
 
 hipError_t launch_mfma_splitk(const Problem &p, hipStream_t s, int tile, int slices, float *ws) {

@@ -151,21 +151,27 @@ hipError_t launch_auto_mfma(const Problem &p, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Split-k with a caller-provided workspace.  Products with few blocks of C and a
 // long k leave most CUs idle (128 x 128 x 65536: 4 blocks of 64 x 64); they split
-// k into slices whose unscaled partial products go to workspace planes, added in
-// slice order by a second kernel (deterministic, no atomics).  The few-rows
-// kernel was tried the same way (512-byte row segments, 16 slices for 1 x 4096 x
-// 4096) and lost to the plain kernel by the second launch, so it never splits.
+// k into slices whose unscaled partial products go to workspace planes, added by
+// a second kernel in an order fixed by the shape (deterministic, no atomics).
+// The few-rows kernel was tried the same way (512-byte row segments, 16 slices
+// for 1 x 4096 x 4096) and lost to the plain kernel by the second launch, so it
+// never splits.
 enum WsKind { WS_NONE = 0, WS_MFMA = 1 };
 struct WsPlan {
     int kind, tile, slices;
 };
 
-constexpr double kReduceBytesPerUs = 2.5e6;
-constexpr double kReduceLaunchUs = 3.0;
+// Cost of the partial planes beyond the product kernel: the planes are written
+// by the product kernel and read back by the reduction (fitted on the same split
+// launches as the product model: 2.5 us fixed, 0.31 us per MB of planes), and at
+// most 64 MiB of planes, which stay in the Infinity Cache between the two.
+constexpr double kSplitFixedUs = 2.5;
+constexpr double kSplitUsPerMB = 0.31;
+constexpr int64_t kSplitMaxPlaneBytes = 64ll << 20;
 
-double reduce_us(const Problem &p, int slices) {
+double split_overhead_us(const Problem &p, int slices) {
     const double plane = 4.0 * p.M * (double)p.N;
-    return kReduceLaunchUs + (slices * plane + plane * (p.beta != 0.0f ? 2 : 1)) / kReduceBytesPerUs;
+    return kSplitFixedUs + (slices * plane + plane * (p.beta != 0.0f ? 2 : 1)) * kSplitUsPerMB / 1e6;
 }
 
 int64_t ws_bytes(const WsPlan &w, const Problem &p) {
@@ -181,16 +187,18 @@ WsPlan plan_workspace(const Problem &p, int algo, int cus) {
     static constexpr int kSplitTiles[] = {1, 4, 5};
     for (int tile : kSplitTiles) {
         const int64_t nwin = ((int64_t)p.K + sgemm::mfma_tile_bk(tile) - 1) / sgemm::mfma_tile_bk(tile);
-        for (int slices = 2; slices <= 128 && 2 * (int64_t)slices <= nwin; slices *= 2) {
+        for (int slices = 2; slices <= 128 && 2 * (int64_t)slices <= nwin &&
+                             (int64_t)slices * p.M * p.N * 4 <= kSplitMaxPlaneBytes;
+             slices *= 2) {
             const double us = sgemm::mfma_model_tile_us(tile, p.M, p.N, p.K, cus, slices) +
-                              reduce_us(p, slices);
+                              split_overhead_us(p, slices);
             if (us < best_us) {
                 best_us = us;
                 best = WsPlan{WS_MFMA, tile, slices};
             }
         }
     }
-    return best_us < 0.8 * whole ? best : none;
+    return best_us < 0.9 * whole ? best : none;
 }
 
 bool handles_transposes(int algo) {

@@ -197,6 +197,12 @@ def test_workspace_size_and_validation():
     for shape in [(8192, 8192, 8192), (2048, 3072, 4096), (1024, 1024, 1024), (1, 4096, 4096),
                   (4096, 1, 4096), (1, 100000, 4096), (0, 5, 5), (5, 5, 0)]:
         assert sg.sgemm_f32_workspace_size(0, 0, *shape) == 0, shape
+    # the planes never exceed 64 MiB, whatever the shape
+    for m in (32, 100, 256, 700, 1024, 1500, 2048, 3000, 4096):
+        for n in (32, 256, 1000, 2048, 4096):
+            for k in (4096, 65536, 1 << 20):
+                need = sg.sgemm_f32_workspace_size(0, 0, m, n, k)
+                assert 0 <= need <= 64 << 20 and need % (4 * m * n) == 0, (m, n, k, need)
     assert sg.sgemm_f32_workspace_size(2, 0, 128, 128, 65536) == 0
     assert sg.sgemm_f32_workspace_size(0, 0, -1, 128, 65536) == 0
     M, N, K = 128, 128, 65536
