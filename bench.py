@@ -353,7 +353,8 @@ def config_report(torch, sg, args):
 TILE_SHAPES = [(8192, 8192, 8192), (2048, 3072, 4096), (4095, 4097, 1023), (1024, 1024, 1024),
                (512, 512, 512), (3000, 2000, 1500), (1000, 5000, 2000), (6000, 6000, 1000),
                (256, 8192, 8192), (8192, 256, 8192), (4096, 4096, 256), (16384, 16384, 1024),
-               (2048, 2048, 2048), (4096, 4096, 4096), (128, 128, 65536)]
+               (2048, 2048, 2048), (4096, 4096, 4096), (128, 128, 65536), (512, 512, 32768),
+               (256, 256, 16384), (512, 512, 4096), (1000, 1000, 8192)]
 
 
 def tile_sweep(torch, sg, shapes, args):

@@ -14,13 +14,15 @@ namespace sgemm {
 // throughput in TFLOP/s, t1 a fixed cost per tile (prologue, epilogue) and t0 a
 // fixed cost per launch.  Each configuration has two throughputs: one for
 // products whose A and B together fit in 200 MB (inside the 256 MB Infinity
-// Cache), one for larger products.  The four numbers per configuration were
-// fitted (least squares on log time) to timings of every configuration on 15
-// shapes on MI355X, among them the 512^3, 1024^3, 2048 x 3072 x 4096,
-// 4095 x 4097 x 1023 and 8192^3 products; on 14 of them the model picks the
-// fastest configuration and on the other one within 1% of it.  The smallest
-// estimate wins.  The timings are of untransposed operands; the other storage
-// orders use the same choice.
+// Cache), one for larger products.  When every CU gets at most one block, the
+// per-block term is at least the block's k windows times a per-window latency
+// (window_floor_us below).  The four numbers per configuration were fitted
+// (least squares on log time) to timings of every configuration on 19 shapes on
+// MI355X, among them the 512^3, 1024^3, 2048 x 3072 x 4096, 4095 x 4097 x 1023
+// and 8192^3 products and four with a long k and few blocks; on 17 of them the
+// model picks the fastest configuration and on the other two one within 0.3% of
+// it.  The smallest estimate wins.  The timings are of untransposed operands;
+// the other storage orders use the same choice.
 struct TileChoice {
     const char *name;  // block, k window, wave block, wave groups, LDS stages
     int bm, bn;
@@ -31,13 +33,14 @@ struct TileChoice {
 };
 
 static constexpr TileChoice kTiles[] = {
-    {"256x256x16 w128x128 k1 s3", 256, 256, 148.5, 150.5, 0.0, 15.0},
-    {"128x128x16 w32x128 k1 s3", 128, 128, 140.5, 141.5, 2.5, 3.0},
-    {"128x192x32 w64x96 k2 s3", 128, 192, 139.0, 137.5, 10.0, 6.0},
-    {"192x128x16 w96x64 k1 s3", 192, 128, 141.0, 143.0, 9.0, 2.0},
-    {"64x64x16 w32x32 k1 s3", 64, 64, 115.0, 115.5, 7.5, 0.0},
-    {"64x64x32 w32x32 k2 s3", 64, 64, 120.5, 119.0, 5.5, 1.0},
-    {"32x32x32 w32x32 k4 s2", 32, 32, 99.0, 100.5, 7.0, 0.0},
+    {"256x256x16 w128x128 k1 s3", 256, 256, 149.0, 150.5, 0.5, 15.0},
+    {"128x128x16 w32x128 k1 s3", 128, 128, 142.5, 145.0, 4.5, 2.0},
+    {"128x192x32 w64x96 k2 s3", 128, 192, 139.0, 139.0, 10.5, 6.0},
+    {"192x128x16 w96x64 k1 s3", 192, 128, 145.0, 146.5, 11.0, 2.0},
+    {"64x64x16 w32x32 k1 s3", 64, 64, 124.0, 122.0, 8.5, 0.0},
+    {"64x64x32 w32x32 k2 s3", 64, 64, 125.5, 127.5, 6.0, 1.0},
+    {"32x32x32 w32x32 k4 s2", 32, 32, 105.0, 107.0, 6.5, 0.0},
+    {"32x32x64 w32x32 k4 s3", 32, 32, 114.0, 108.0, 5.5, 2.0},
 };
 static_assert(sizeof(kTiles) / sizeof(kTiles[0]) == kTileCount, "one entry per configuration");
 // The table rows follow the launcher tables of mfma_kernel.h.
@@ -48,6 +51,7 @@ static_assert(kTiles[3].bm == TileTall::BM && kTiles[3].bn == TileTall::BN, "row
 static_assert(kTiles[4].bm == TileSmall::BM && kTiles[4].bn == TileSmall::BN, "row 4");
 static_assert(kTiles[5].bm == TileSplit64::BM && kTiles[5].bn == TileSplit64::BN, "row 5");
 static_assert(kTiles[6].bm == TileTiny::BM && kTiles[6].bn == TileTiny::BN, "row 6");
+static_assert(kTiles[7].bm == TileTiny64::BM && kTiles[7].bn == TileTiny64::BN, "row 7");
 
 int compute_units() {
     int dev = 0, cus = 0;
@@ -152,6 +156,7 @@ int mfma_tile_bk(int tile) {
     case 4: return TileSmall::BK;
     case 5: return TileSplit64::BK;
     case 6: return TileTiny::BK;
+    case 7: return TileTiny64::BK;
     default: return 0;
     }
 }

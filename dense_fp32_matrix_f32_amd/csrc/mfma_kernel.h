@@ -747,8 +747,14 @@ using TileSmall = MfmaTile<64, 64, 16, 32, 32, 1, 4, 3>;
 using TileSplit64 = MfmaTile<64, 64, 32, 32, 32, 2, 4, 3>;
 // k split four ways: one 8-wide step per group and window, so two stages.
 using TileTiny = MfmaTile<32, 32, 32, 32, 32, 4, 4, 2>;
+// The same block with 64-wide windows and three stages: twice the work per
+// window and one more window in flight, for grids of at most one block per CU
+// over a long k, where TileTiny waits on its loads (512 x 512 x 32768: 352 ->
+// 230 us).  Its 57 KB of LDS allow two blocks per CU, so many-block grids stay
+// with TileTiny.
+using TileTiny64 = MfmaTile<32, 32, 64, 32, 32, 4, 4, 3>;
 
-constexpr int kTileCount = 7;
+constexpr int kTileCount = 8;
 
 // Launch configuration `tile` (0 <= tile < kTileCount, in the order above) for
 // one storage order (defined in mfma_nn.hip, mfma_nt.hip, mfma_tn.hip, mfma_tt.hip).
@@ -773,6 +779,7 @@ hipError_t launch_mfma_tt_splitk(const Problem &p, hipStream_t s, int tile, int 
         case 4: return launch_tile<TileSmall, TA, TB>(p, s);                                  \
         case 5: return launch_tile<TileSplit64, TA, TB>(p, s);                                \
         case 6: return launch_tile<TileTiny, TA, TB>(p, s);                                   \
+        case 7: return launch_tile<TileTiny64, TA, TB>(p, s);                                 \
         default: return hipErrorInvalidValue;                                                 \
         }                                                                                     \
     }                                                                                         \
