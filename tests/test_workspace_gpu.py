@@ -91,3 +91,39 @@ def test_matmul_helper_workspace():
         C = sg.matmul(At, Bt, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(C.cpu().numpy().astype(np.float64), want)
+
+
+def _reduce_groups(M, N, slices):
+    """Plane groups per output element of the reduction for this plan: the fewest
+    (up to 16, at most `slices`) that give 2048 work-groups of 256 work-items."""
+    g = 1
+    while g < 16 and 2 * g <= slices and (M * N * g + 255) // 256 < 2048:
+        g *= 2
+    return g
+
+
+# one shape per plane grouping of the reduction (1, 2, 4, 8, 16 groups per element)
+GROUP_CASES = [(1024, 512, 8192, 1), (512, 512, 32768, 2), (384, 384, 16384, 4),
+               (256, 256, 16384, 8), (128, 128, 65536, 16)]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}-g{c[3]}")
+def test_reduction_groupings(case):
+    """Every plane grouping of the reduction, on sampled outputs: whole rows and
+    columns at both edges and a seeded scatter, with alpha and beta."""
+    M, N, K, groups = case
+    need = sg.sgemm_f32_workspace_size(N_, N_, M, N, K)
+    assert need > 0 and need % (4 * M * N) == 0, "the plan no longer splits this shape"
+    slices = need // (4 * M * N)
+    assert _reduce_groups(M, N, slices) == groups, (slices, "the plan no longer gives this grouping")
+    torch, As, Bs, C0, dA, dB = _setup(M, N, K, N_, N_, "normal", 900 + groups)
+    log(f"[gpu] split-k reduction {M}x{N}x{K}, {slices} slices, {groups} groups")
+    C, _ = _run_ws(torch, dA, dB, C0, M, N, K, N_, N_, 0.5, 2.0, need // 4)
+    rng = np.random.default_rng(groups)
+    rows = np.concatenate([np.repeat([0, M - 1], N), np.tile(np.arange(M), 2),
+                           rng.integers(0, M, 4096)])
+    cols = np.concatenate([np.tile(np.arange(N), 2), np.repeat([0, N - 1], M),
+                           rng.integers(0, N, 4096)])
+    want, S = oracle.sgemm_ex(As, Bs, False, False, 0.5, 2.0, C0, rows=rows, cols=cols)
+    ex = oracle.excess(C[rows, cols], want, S)
+    assert np.all(ex <= 1.0), f"{int(np.count_nonzero(ex > 1))} sampled elements beyond tolerance"
