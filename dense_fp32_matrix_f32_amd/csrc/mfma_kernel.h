@@ -553,6 +553,21 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
     const int col0 = strip_n + (C::TB ? lr : C::TN * lr);
     auto col_of = [&](int j) { return col0 + (C::TB ? 32 * j : j); };
     auto put = [&](float *dst, float v) { *dst = epilogue(v, alpha, beta, dst); };
+    // mn-contiguous B: the lane's TN adjacent columns of row r of block row i as one
+    // access (read-modify-write when beta != 0).
+    auto put_row = [&](float *dst, int i, int r) {
+        float v[C::TN];
+        if (beta == 0.0f) {
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) v[j] = alpha * acc[i][j][r];
+        } else {
+            float old[C::TN];
+            __builtin_memcpy(old, dst + col0, sizeof(old));
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) v[j] = fmaf(beta, old[j], alpha * acc[i][j][r]);
+        }
+        __builtin_memcpy(dst + col0, v, sizeof(v));
+    };
     if (full) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
@@ -560,17 +575,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
             for (int r = 0; r < 16; ++r) {
                 float *dst = Cm + (int64_t)row_of(i, r) * ldc;
                 if constexpr (!C::TB) {
-                    float v[C::TN];
-                    if (beta == 0.0f) {
-#pragma unroll
-                        for (int j = 0; j < C::TN; ++j) v[j] = alpha * acc[i][j][r];
-                    } else {
-                        float old[C::TN];
-                        __builtin_memcpy(old, dst + col0, sizeof(old));
-#pragma unroll
-                        for (int j = 0; j < C::TN; ++j) v[j] = fmaf(beta, old[j], alpha * acc[i][j][r]);
-                    }
-                    __builtin_memcpy(dst + col0, v, sizeof(v));
+                    put_row(dst, i, r);
                 } else {
 #pragma unroll
                     for (int j = 0; j < C::TN; ++j) put(dst + col_of(j), acc[i][j][r]);
@@ -580,6 +585,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
+        // Edge blocks skip rows >= M; a lane whose TN adjacent columns all lie
+        // inside C still stores them as one access (a block past M only, such as
+        // the last block row of a 4095-row product, then stores as fast as the
+        // others: all blocks finish together, so one slow epilogue delays them all).
+        const bool row_inside = !C::TB && col0 + C::TN <= N;
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
@@ -587,9 +597,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
                 const int row = row_of(i, r);
                 if (row < M) {
                     float *dst = Cm + (int64_t)row * ldc;
+                    if (row_inside) {
+                        if constexpr (!C::TB) put_row(dst, i, r);
+                    } else {
 #pragma unroll
-                    for (int j = 0; j < C::TN; ++j)
-                        if (col_of(j) < N) put(dst + col_of(j), acc[i][j][r]);
+                        for (int j = 0; j < C::TN; ++j)
+                            if (col_of(j) < N) put(dst + col_of(j), acc[i][j][r]);
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
