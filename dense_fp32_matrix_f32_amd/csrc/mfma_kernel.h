@@ -688,7 +688,7 @@ bool narrow_offsets(const Problem &p) {
 // Split-k form: work-group b computes block b % tiles over slice b / tiles of the
 // k windows (slice q of S covers windows [q*W/S, (q+1)*W/S)) and stores its
 // partial block, unscaled, to plane q of the workspace (M x N, row stride N).
-// The planes are added in slice order by splitk_reduce (basic.hip).
+// splitk_reduce_kernel (basic.hip) adds the planes in an order fixed by the shape.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_splitk_kernel(GemmArgs g, int tiles_m,
                                                                         int tiles_n, int slices,

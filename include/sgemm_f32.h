@@ -213,11 +213,12 @@ hipError_t sgemm_f32_ex_mfma_tile(int transa, int transb, int M, int N, int K, f
  * the first kernel writes each slice's unscaled partial product to a plane of
  * the workspace (S planes of M x N floats, row stride N), the second forms
  *     C = alpha * (plane 0 + plane 1 + ... + plane S-1) + beta * C
- * adding the planes in slice order, so results are reproducible run to run
- * (they differ from sgemm_f32_ex() only in summation order, within the same
- * bound).  The choice of S and of the block configuration comes from the same
- * cost model as the rest of the automatic choice; the split is taken only when
- * modelled at least 20% faster.
+ * adding the planes in an order fixed by (M, N, S), so results are
+ * reproducible run to run (they differ from sgemm_f32_ex() only in summation
+ * order, within the same bound).  The choice of S and of the block
+ * configuration comes from the same cost model as the rest of the automatic
+ * choice; the split is taken only when modelled at least 10% faster, and the
+ * planes never take more than 64 MiB.
  *
  * sgemm_f32_workspace_size()  bytes sgemm_f32_ex_ws() would use for these
  *                             arguments on the current device (0: no split;
