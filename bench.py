@@ -433,7 +433,7 @@ def main(argv=None):
     args = p.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the product runs on one GPU; sharding across GPUs is not implemented, so --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
