@@ -193,3 +193,35 @@ def test_torch_helper_transposed_views_and_scaling():
         assert np.array_equal(out.cpu().numpy().astype(np.int64), exact)
     with pytest.raises(ValueError):
         sg.matmul(Xd, Yd, beta=1.0)
+
+
+def _sweep_cases(n=48, seed=2024):
+    """Seeded shapes for the automatic choice: sizes log-uniform over 1..1500 (every
+    dimension below 9 a quarter of the time, so the few-row and few-column kernels
+    and the edge strips come up), any storage order, padded row strides, and one of
+    three alpha/beta pairs."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dims = []
+        for _ in range(3):
+            if rng.random() < 0.25:
+                dims.append(int(rng.integers(1, 9)))
+            else:
+                dims.append(int(np.exp(rng.uniform(np.log(9), np.log(1500)))))
+        ta, tb = (int(x) for x in rng.integers(0, 2, 2))
+        ab = [(1.0, 0.0), (2.0, -1.0), (0.5, 0.25)][int(rng.integers(0, 3))]
+        pads = (int(rng.integers(0, 6)), int(rng.integers(0, 6)))
+        cases.append((i, *dims, ta, tb, *ab, *pads))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}")
+def test_random_shapes_automatic_choice(case):
+    """The automatic choice on seeded random shapes, bitwise on small integers (the
+    alpha/beta pairs are exact in fp32 on integer data)."""
+    _, M, N, K, ta, tb, alpha, beta, pad_a, pad_b = case
+    As, Bs, C0 = _operands(M, N, K, "smallint", 700 + case[0], ta, tb, pad_a, pad_b)
+    C = _run(As, Bs, M, N, K, ta, tb, alpha, beta, C0)
+    check_ex(As, Bs, M, N, K, ta, tb, alpha, beta, C0, C,
+             f"auto {lid((ta, tb))} {M}x{N}x{K}", exact=True)
