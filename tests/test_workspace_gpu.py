@@ -127,3 +127,31 @@ def test_reduction_groupings(case):
     want, S = oracle.sgemm_ex(As, Bs, False, False, 0.5, 2.0, C0, rows=rows, cols=cols)
     ex = oracle.excess(C[rows, cols], want, S)
     assert np.all(ex <= 1.0), f"{int(np.count_nonzero(ex > 1))} sampled elements beyond tolerance"
+
+
+def _ws_sweep(n=12, seed=77):
+    """Seeded shapes with few blocks of C and a long k: M, N in 1..300, K in 2000..30000,
+    any storage order, one of three alpha/beta pairs."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M, N = (int(x) for x in rng.integers(1, 301, 2))
+        K = int(rng.integers(2000, 30001))
+        ta, tb = (int(x) for x in rng.integers(0, 2, 2))
+        ab = [(1.0, 0.0), (2.0, -1.0), (0.5, 0.25)][int(rng.integers(0, 3))]
+        out.append((i, M, N, K, ta, tb, *ab))
+    return out
+
+
+@pytest.mark.parametrize("case", _ws_sweep(), ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}")
+def test_random_shapes_with_workspace(case):
+    """sgemm_f32_ex_ws with the workspace it asks for, split or not, bitwise on small
+    integers; the workspace past the planned bytes stays untouched."""
+    i, M, N, K, ta, tb, alpha, beta = case
+    need = sg.sgemm_f32_workspace_size(ta, tb, M, N, K)
+    torch, As, Bs, C0, dA, dB = _setup(M, N, K, ta, tb, "smallint", 1000 + i)
+    log(f"[gpu] split-k sweep {M}x{N}x{K} {ta}{tb} alpha={alpha} beta={beta} workspace {need} B")
+    C, ws = _run_ws(torch, dA, dB, C0, M, N, K, ta, tb, alpha, beta, need // 4 + 64)
+    assert np.all(ws[need // 4:] == np.float32(SENT)), "workspace written past the planned bytes"
+    want, _ = oracle.sgemm_ex(As, Bs, ta, tb, alpha, beta, C0)
+    assert np.array_equal(C.astype(np.float64), want)
