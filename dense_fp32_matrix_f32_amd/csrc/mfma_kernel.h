@@ -530,11 +530,14 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
     }
 }
 
-// Store the accumulators of block (m0, n0) to C; rows >= M and columns >= N are
-// skipped.  Accumulator r of block (i, j) holds MFMA row rho = 8*(r/4) + 4*lh +
-// r%4 and MFMA column lr of that block, placed as described in the header.
+// Store the accumulators of block (m0, n0) to C; rows outside [m_lo, M) and
+// columns outside [n_lo, N) are skipped (m_lo > m0 or n_lo > n0 for a block
+// moved back from the edge, whose first rows or columns belong to its
+// neighbour).  Accumulator r of block (i, j) holds MFMA row rho = 8*(r/4) +
+// 4*lh + r%4 and MFMA column lr of that block, placed as described in the header.
 template <class C>
-__device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, const Acc<C> &acc) {
+__device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, const Acc<C> &acc,
+                                           int m_lo, int n_lo) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 31, lh = lane >> 5;
     const int sw = wave % C::SPATIAL;
@@ -543,7 +546,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
     float *__restrict__ Cm = g.C;
     const int64_t ldc = g.ldc;
     const float alpha = g.alpha, beta = g.beta;
-    const bool full = (m0 + C::BM <= M) && (n0 + C::BN <= N);
+    const bool full = (m0 + C::BM <= M) && (n0 + C::BN <= N) && m_lo == m0 && n_lo == n0;
     const int strip_m = m0 + wm * C::WM, strip_n = n0 + wn * C::WN;
     auto row_of = [&](int i, int r) {
         const int rho = 8 * (r >> 2) + 4 * lh + (r & 3);
@@ -585,24 +588,26 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
-        // Edge blocks skip rows >= M; a lane whose TN adjacent columns all lie
-        // inside C still stores them as one access (a block past M only, such as
-        // the last block row of a 4095-row product, then stores as fast as the
-        // others: all blocks finish together, so one slow epilogue delays them all).
-        const bool row_inside = !C::TB && col0 + C::TN <= N;
+        // Edge blocks skip rows outside [m_lo, M); a lane whose TN adjacent
+        // columns all lie inside [n_lo, N) still stores them as one access (a
+        // block past M only, such as the last block row of a 4095-row product,
+        // then stores as fast as the others: all blocks finish together, so one
+        // slow epilogue delays them all).
+        const bool row_inside = !C::TB && col0 >= n_lo && col0 + C::TN <= N;
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = row_of(i, r);
-                if (row < M) {
+                if (row >= m_lo && row < M) {
                     float *dst = Cm + (int64_t)row * ldc;
                     if (row_inside) {
                         if constexpr (!C::TB) put_row(dst, i, r);
                     } else {
 #pragma unroll
                         for (int j = 0; j < C::TN; ++j)
-                            if (col_of(j) < N) put(dst + col_of(j), acc[i][j][r]);
+                            if (col_of(j) >= n_lo && col_of(j) < N)
+                                put(dst + col_of(j), acc[i][j][r]);
                     }
                 }
             }
@@ -658,6 +663,20 @@ __device__ __forceinline__ void zero_acc(Acc<C> &acc) {
         for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
 }
 
+// A block that reaches past M on an m-contiguous op(A), or past N on an
+// n-contiguous op(B), would have to load that operand element by element with
+// clamped indices; all blocks of a launch finish together, so that one slow
+// block row or column sets the time of the launch.  When the matrix holds a
+// whole block in that direction, the block is moved back to end exactly at M
+// (or N): it computes BM x BN outputs entirely inside C with whole 16-byte
+// loads, and stores only from its original first row (column) on, the rows
+// before that belonging to its neighbour.
+template <class C>
+__device__ __forceinline__ void edge_origin(int M, int N, int &m0, int &n0) {
+    if (C::TA && m0 + C::BM > M && M >= C::BM) m0 = M - C::BM;
+    if (!C::TB && n0 + C::BN > N && N >= C::BN) n0 = N - C::BN;
+}
+
 // Data-parallel form: one work-group per BM x BN block of C.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_kernel(GemmArgs g, int tiles_m,
@@ -665,12 +684,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_kernel(GemmArgs g, in
     __shared__ __attribute__((aligned(16))) float lds[C::LDS_FLOATS];
     int tm, tn;
     tile_order(blockIdx.x, tiles_m, tiles_n, C::GROUP_M, &tm, &tn);
-    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int m_lo = tm * C::BM, n_lo = tn * C::BN;
+    int m0 = m_lo, n0 = n_lo;
+    edge_origin<C>(g.M, g.N, m0, n0);
     Acc<C> acc;
     zero_acc<C>(acc);
     mma_tile<C>(g, lds, m0, n0, 0, (g.K + C::BK - 1) / C::BK, acc);
     if (!kw_reduce<C>(lds, acc)) return;
-    store_tile<C>(g, m0, n0, acc);
+    store_tile<C>(g, m0, n0, acc, m_lo, n_lo);
 }
 
 // True when every per-lane byte offset from a block's first row or column
@@ -698,7 +719,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_splitk_kernel(GemmArg
     const int t = blockIdx.x % tiles, slice = blockIdx.x / tiles;
     int tm, tn;
     group_tile(t, tiles_m, tiles_n, C::GROUP_M, &tm, &tn);
-    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int m_lo = tm * C::BM, n_lo = tn * C::BN;
+    int m0 = m_lo, n0 = n_lo;
+    edge_origin<C>(g.M, g.N, m0, n0);
     const int nwin = (g.K + C::BK - 1) / C::BK;
     const int wb = (int)((int64_t)slice * nwin / slices);
     const int we = (int)((int64_t)(slice + 1) * nwin / slices);
@@ -711,7 +734,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_splitk_kernel(GemmArg
     o.ldc = g.N;
     o.alpha = 1.0f;
     o.beta = 0.0f;
-    store_tile<C>(o, m0, n0, acc);
+    store_tile<C>(o, m0, n0, acc, m_lo, n_lo);
 }
 
 template <class T, bool TA, bool TB>
