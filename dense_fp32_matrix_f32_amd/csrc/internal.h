@@ -62,7 +62,15 @@ int compute_units();
 // The fp32 product on the bf16 matrix cores with three-part operand splitting
 // (untransposed operands only).
 hipError_t launch_split(const Problem &p, hipStream_t s);
-hipError_t launch_skinny(const Problem &p, hipStream_t s);
+// Streaming kernels for products with few rows of C (any number of rows, in
+// passes of 8): launch_skinny_rows (skinny.hip) when B is not transposed,
+// launch_skinny_rows_tb (skinny_n.hip, on C^T = B^T * op(A)^T) when it is; and
+// with few columns of C (passes of 8): launch_skinny_cols (skinny_n.hip) when A
+// is not transposed, launch_skinny_cols_ta (skinny.hip, on C^T) when it is.
+hipError_t launch_skinny_rows(const Problem &p, hipStream_t s);
+hipError_t launch_skinny_rows_tb(const Problem &p, hipStream_t s);
+hipError_t launch_skinny_cols(const Problem &p, hipStream_t s);
+hipError_t launch_skinny_cols_ta(const Problem &p, hipStream_t s);
 // Split-k: `slices` unscaled partial products of op(A)*op(B) go to the workspace
 // planes ws[q*M*N + i*N + j], then launch_splitk_reduce() forms
 // C = alpha * (sum over q) + beta * C, adding the planes in an order fixed by
@@ -76,6 +84,5 @@ hipError_t launch_splitk_reduce(const Problem &p, int slices, const float *ws, h
 double mfma_model_tile_us(int tile, int M, int N, int K, int cus, int slices);
 // k window of configuration `tile` (0 for an unknown id).
 int mfma_tile_bk(int tile);
-hipError_t launch_skinny_n(const Problem &p, hipStream_t s);
 
 }  // namespace sgemm

@@ -44,16 +44,26 @@ hipError_t validate(int transa, int transb, int M, int N, int K, float alpha, co
     return hipSuccess;
 }
 
-// Untransposed products with few rows or few columns stream one operand and are
-// bound by memory, so the streaming kernels win; everything else goes to the
-// matrix cores.
+// Products with few rows or few columns stream one operand and are bound by
+// memory, so the streaming kernels win; everything else goes to the matrix
+// cores.
 int choose(int transa, int transb, int M, int N, int K) {
+    (void)transa;
+    (void)transb;
     (void)K;
-    if (transa == SGEMM_F32_OP_N && transb == SGEMM_F32_OP_N) {
-        if (M <= 8) return SGEMM_F32_ALGO_SKINNY;
-        if (N <= 8) return SGEMM_F32_ALGO_SKINNY_N;
-    }
+    if (M <= 8) return SGEMM_F32_ALGO_SKINNY;
+    if (N <= 8) return SGEMM_F32_ALGO_SKINNY_N;
     return SGEMM_F32_ALGO_MFMA;
+}
+
+// Few rows (columns) of C in any storage order: the streaming kernel whose
+// streamed operand runs along memory (see internal.h).
+hipError_t launch_few_rows(const Problem &p, hipStream_t s) {
+    return p.tb ? sgemm::launch_skinny_rows_tb(p, s) : sgemm::launch_skinny_rows(p, s);
+}
+
+hipError_t launch_few_cols(const Problem &p, hipStream_t s) {
+    return p.ta ? sgemm::launch_skinny_cols_ta(p, s) : sgemm::launch_skinny_cols(p, s);
 }
 
 // Automatic choice for the products the matrix cores take.  When N lies a few
@@ -62,29 +72,21 @@ int choose(int transa, int transb, int M, int N, int K) {
 // for a sliver of work (4095 x 4097: 726 blocks of 192 x 128 for 4095 x 4096
 // plus one column).  The product is then split: the blocks cover the leading
 // multiple of 32 and the strip that is left goes to a kernel sized for it (the
-// streaming kernels for untransposed operands, the matrix cores otherwise), when
-// the cost model of the tile table says the launches together finish sooner.
+// streaming kernels), when the cost model of the tile table says the launches
+// together finish sooner.
 // Every element of C is still computed whole by exactly one kernel.
 constexpr int kPeelMax = 8;    // widest strip split off
 constexpr double kStreamBytesPerUs = 2.5e6;  // streaming kernels on small strips
 constexpr double kStreamLaunchUs = 4.0;
 
 // Modelled time of a rows x cols strip over the whole k range.
-double strip_us(const Problem &p, int rows, int cols, int cus) {
-    if (!p.ta && !p.tb) {
-        const double bytes =
-            4.0 * ((double)rows * p.K + (double)p.K * cols + (double)rows * cols);
-        return kStreamLaunchUs + bytes / kStreamBytesPerUs;
-    }
-    return sgemm::mfma_model_us(rows, cols, p.K, cus);
+double strip_us(const Problem &p, int rows, int cols) {
+    const double bytes = 4.0 * ((double)rows * p.K + (double)p.K * cols + (double)rows * cols);
+    return kStreamLaunchUs + bytes / kStreamBytesPerUs;
 }
 
 hipError_t launch_strip(const Problem &q, hipStream_t s) {
-    if (!q.ta && !q.tb) {
-        if (q.M <= kPeelMax) return sgemm::launch_skinny(q, s);
-        return sgemm::launch_skinny_n(q, s);
-    }
-    return sgemm::launch_mfma(q, s);
+    return q.M <= kPeelMax ? launch_few_rows(q, s) : launch_few_cols(q, s);
 }
 
 // Columns [n0, N) of op(B) and C, all rows.
@@ -127,8 +129,8 @@ Split plan_split(const Problem &p, int cus) {
         if ((pn && !cut_n) || (pm && !cut_m)) continue;
         const Split sp{pm ? p.M - rm : p.M, pn ? p.N - rn : p.N};
         double us = sgemm::mfma_model_us(sp.m_main, sp.n_main, p.K, cus);
-        if (pn) us += strip_us(p, p.M, rn, cus);
-        if (pm) us += strip_us(p, rm, sp.n_main, cus);
+        if (pn) us += strip_us(p, p.M, rn);
+        if (pm) us += strip_us(p, rm, sp.n_main);
         if (us < best_us) {
             best = sp;
             best_us = us;
@@ -203,7 +205,8 @@ WsPlan plan_workspace(const Problem &p, int algo, int cus) {
 
 bool handles_transposes(int algo) {
     return algo == SGEMM_F32_ALGO_AUTO || algo == SGEMM_F32_ALGO_NAIVE ||
-           algo == SGEMM_F32_ALGO_LDS_TILED || algo == SGEMM_F32_ALGO_MFMA;
+           algo == SGEMM_F32_ALGO_LDS_TILED || algo == SGEMM_F32_ALGO_MFMA ||
+           algo == SGEMM_F32_ALGO_SKINNY || algo == SGEMM_F32_ALGO_SKINNY_N;
 }
 
 Problem problem(int transa, int transb, int M, int N, int K, float alpha, const float *A,
@@ -295,8 +298,8 @@ extern "C" hipError_t sgemm_f32_ex_algo(int transa, int transb, int M, int N, in
     case SGEMM_F32_ALGO_LDS_TILED: return sgemm::launch_lds_tiled(p, stream);
     case SGEMM_F32_ALGO_VALU_REGBLOCK: return sgemm::launch_valu_regblock(p, stream);
     case SGEMM_F32_ALGO_MFMA: return sgemm::launch_mfma(p, stream);
-    case SGEMM_F32_ALGO_SKINNY: return sgemm::launch_skinny(p, stream);
-    case SGEMM_F32_ALGO_SKINNY_N: return sgemm::launch_skinny_n(p, stream);
+    case SGEMM_F32_ALGO_SKINNY: return launch_few_rows(p, stream);
+    case SGEMM_F32_ALGO_SKINNY_N: return launch_few_cols(p, stream);
     case SGEMM_F32_ALGO_BF16X6: return sgemm::launch_split(p, stream);
     default: return hipErrorInvalidValue;
     }

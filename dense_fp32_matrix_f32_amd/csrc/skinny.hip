@@ -11,6 +11,12 @@
 // bytes of a row) two work-groups share every 128-byte line, so strips are
 // assigned XCD by XCD: neighbouring strips run on the same XCD and a line comes
 // through its L2 once, not once per XCD.
+//
+// In general terms the kernel forms out[m][n] = alpha * sum_k x[m][k] * Y[k][n]
+// + beta * out[m][n] for at most 8 rows m, with Y row-major (streamed) and x and
+// out given by element strides, which covers every storage order: op(A) * B for
+// few rows of C when B is not transposed, and (op(A) * op(B))^T = op(B)^T *
+// A^T for few columns of C when A is transposed (Y is then the stored A).
 #include <type_traits>
 
 #include "internal.h"
@@ -28,11 +34,14 @@ __device__ __forceinline__ f32x4 load16_skinny(const float *p) {
 }
 
 // THREADS work-items; LPR of them share one row segment of 4*LPR columns, so
-// there are S = THREADS/LPR k slots.  MR is the number of rows of A handled.
-template <int MR, int LPR, int THREADS>
+// there are S = THREADS/LPR k slots.  MR is the number of rows of x handled.
+// x[m][k] = A[m*xm + k*xk] (XK1: xk == 1), Y[k][n] = B[k*ldb + n], out[m][n] =
+// C[m*cm + n*cn].
+template <int MR, int LPR, int THREADS, bool XK1>
 __global__ __launch_bounds__(THREADS) void skinny_kernel(
-    int M, int N, int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
-    int64_t ldb, float *__restrict__ C, int64_t ldc, float alpha, float beta) {
+    int M, int N, int K, const float *__restrict__ A, int64_t xm, int64_t xk,
+    const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t cm, int64_t cn,
+    float alpha, float beta) {
     constexpr int CW = 4 * LPR;        // columns per work-group
     constexpr int S = THREADS / LPR;   // k slots (a power of two)
     constexpr int OUT = MR * CW;       // outputs per work-group
@@ -48,7 +57,14 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
 
     const float *arow[MR];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) arow[m] = A + (int64_t)min(m, M - 1) * lda;
+    for (int m = 0; m < MR; ++m) arow[m] = A + (int64_t)min(m, M - 1) * xm;
+    auto xat = [&](int m, int k) -> float {
+        if constexpr (XK1) {
+            return arow[m][k];
+        } else {
+            return arow[m][(int64_t)k * xk];
+        }
+    };
 
     float acc[MR][4];
 #pragma unroll
@@ -95,7 +111,7 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int m = 0; m < MR; ++m) a[u][m] = arow[m][k + u * S];
+                for (int m = 0; m < MR; ++m) a[u][m] = xat(m, k + u * S);
 #pragma unroll
             for (int u = 0; u < U; ++u) fma4(a[u], b[u]);
         }
@@ -103,7 +119,7 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
             const f32x4 b = load_b(k);
             float a[MR];
 #pragma unroll
-            for (int m = 0; m < MR; ++m) a[m] = arow[m][k];
+            for (int m = 0; m < MR; ++m) a[m] = xat(m, k);
             fma4(a, b);
         }
     };
@@ -131,44 +147,78 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
     for (int o = tid; o < OUT; o += THREADS) {
         const int m = o / CW, c = o % CW;
         if (m < M && n0 + c < N) {
-            float *dst = C + (int64_t)m * ldc + n0 + c;
+            float *dst = C + (int64_t)m * cm + (int64_t)(n0 + c) * cn;
             *dst = epilogue(red[0][o], alpha, beta, dst);
         }
     }
 }
 
-template <int MR, int THREADS>
-static hipError_t launch_rows(const Problem &p, hipStream_t s) {
+// One streaming product as above: x (rows x K, strides xm, xk), Y (K x cols,
+// row stride ldy), out (rows x cols, strides cm, cn).
+struct RowStream {
+    int rows, cols, K;
+    const float *x;
+    int64_t xm, xk;
+    const float *Y;
+    int64_t ldy;
+    float *out;
+    int64_t cm, cn;
+    float alpha, beta;
+};
+
+template <int MR, int THREADS, bool XK1>
+static hipError_t launch_rows(const RowStream &q, hipStream_t s) {
     // Wide segments give longer contiguous row reads; narrow ones give more
     // work-groups.  Keep at least 256 work-groups (one per CU) when N allows.
-    if (p.N >= 64 * 256) {
-        const int64_t groups = (p.N + 63) / 64;
-        return launch(skinny_kernel<MR, 16, THREADS>, dim3((unsigned)groups), dim3(THREADS), 0, s,
-                      p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta);
+    if (q.cols >= 64 * 256) {
+        const int64_t groups = (q.cols + 63) / 64;
+        return launch(skinny_kernel<MR, 16, THREADS, XK1>, dim3((unsigned)groups), dim3(THREADS),
+                      0, s, q.rows, q.cols, q.K, q.x, q.xm, q.xk, q.Y, q.ldy, q.out, q.cm, q.cn,
+                      q.alpha, q.beta);
     }
-    const int64_t groups = (p.N + 15) / 16;
-    return launch(skinny_kernel<MR, 4, THREADS>, dim3((unsigned)groups), dim3(THREADS), 0, s, p.M,
-                  p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta);
+    const int64_t groups = (q.cols + 15) / 16;
+    return launch(skinny_kernel<MR, 4, THREADS, XK1>, dim3((unsigned)groups), dim3(THREADS), 0, s,
+                  q.rows, q.cols, q.K, q.x, q.xm, q.xk, q.Y, q.ldy, q.out, q.cm, q.cn, q.alpha,
+                  q.beta);
 }
 
-hipError_t launch_skinny(const Problem &p, hipStream_t s) {
-    if ((int64_t)(p.N + 15) / 16 > INT32_MAX) return hipErrorInvalidValue;
+template <bool XK1>
+static hipError_t launch_rows_of(const RowStream &q, hipStream_t s) {
+    // Group sizes measured on 1..8 x 4096 x 4096 with B resident in the
+    // Infinity Cache and streamed from HBM.
+    if (q.rows == 1) return launch_rows<1, 256, XK1>(q, s);
+    if (q.rows == 2) return launch_rows<2, 512, XK1>(q, s);
+    if (q.rows <= 4) return launch_rows<4, 512, XK1>(q, s);
+    return launch_rows<8, 256, XK1>(q, s);
+}
+
+static hipError_t launch_row_stream(const RowStream &p, hipStream_t s) {
+    if ((int64_t)(p.cols + 15) / 16 > INT32_MAX) return hipErrorInvalidValue;
     // More than 8 rows: one pass per group of 8 rows.
-    for (int r0 = 0; r0 < p.M; r0 += SKINNY_MAX_ROWS) {
-        Problem q = p;
-        q.M = p.M - r0 < SKINNY_MAX_ROWS ? p.M - r0 : SKINNY_MAX_ROWS;
-        q.A = p.A + (int64_t)r0 * p.lda;
-        q.C = p.C + (int64_t)r0 * p.ldc;
-        hipError_t e;
-        // Group sizes measured on 1..8 x 4096 x 4096 with B resident in the
-        // Infinity Cache and streamed from HBM.
-        if (q.M == 1) e = launch_rows<1, 256>(q, s);
-        else if (q.M == 2) e = launch_rows<2, 512>(q, s);
-        else if (q.M <= 4) e = launch_rows<4, 512>(q, s);
-        else e = launch_rows<8, 256>(q, s);
+    for (int r0 = 0; r0 < p.rows; r0 += SKINNY_MAX_ROWS) {
+        RowStream q = p;
+        q.rows = p.rows - r0 < SKINNY_MAX_ROWS ? p.rows - r0 : SKINNY_MAX_ROWS;
+        q.x = p.x + (int64_t)r0 * p.xm;
+        q.out = p.out + (int64_t)r0 * p.cm;
+        const hipError_t e = q.xk == 1 ? launch_rows_of<true>(q, s) : launch_rows_of<false>(q, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Few rows of C with B not transposed: x = op(A), Y = B, out = C.
+hipError_t launch_skinny_rows(const Problem &p, hipStream_t s) {
+    const RowStream q{p.M, p.N, p.K, p.A, p.ta ? 1 : p.lda, p.ta ? p.lda : 1, p.B, p.ldb,
+                      p.C, p.ldc, 1, p.alpha, p.beta};
+    return launch_row_stream(q, s);
+}
+
+// Few columns of C with A transposed: C^T = op(B)^T * A^T, so x = op(B)^T
+// (N x K), Y = the stored K x M array A, out = C^T.
+hipError_t launch_skinny_cols_ta(const Problem &p, hipStream_t s) {
+    const RowStream q{p.N, p.M, p.K, p.B, p.tb ? p.ldb : 1, p.tb ? 1 : p.ldb, p.A, p.lda,
+                      p.C, 1, p.ldc, p.alpha, p.beta};
+    return launch_row_stream(q, s);
 }
 
 }  // namespace sgemm

@@ -9,6 +9,13 @@
 // reused for all RW rows.  The 64 per-lane partial sums of each output are added
 // by a fixed butterfly across the wave (lane 0's total is the result), so the
 // result is reproducible run to run and no atomics are involved.
+//
+// In general terms the kernel forms out[i][j] = alpha * sum_k X[i][k] * y[k][j]
+// + beta * out[i][j] for at most 8 columns j, with X's rows contiguous along k
+// (streamed) and y and out given by element strides, which covers every storage
+// order: A * op(B) for few columns of C when A is not transposed, and
+// (op(A) * op(B))^T = B^T * op(A)^T for few rows of C when B is transposed (X is
+// then the stored N x K array B: a row vector times a transposed weight matrix).
 #include "internal.h"
 
 namespace sgemm {
@@ -24,12 +31,17 @@ __device__ __forceinline__ f32x4 load16_n(const float *p) {
 }
 
 // NR columns handled (N <= NR), RW rows per wave, 4 waves per work-group.
-template <int NR, int RW>
+// X[i][k] = A[i*lda + k], y[k][j] = B[k*yk + j*yj], out[i][j] = C[i*ci + j*cj].
+// YM: how a lane reads its four k of y: 0 one value at a time, 1 whole rows of y
+// as 16-byte loads (yj == 1 and N == NR >= 4), 2 four consecutive k of each
+// column as one 16-byte load (yk == 1).
+template <int NR, int RW, int YM>
 __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                                                        const float *__restrict__ A, int64_t lda,
-                                                       const float *__restrict__ B, int64_t ldb,
-                                                       float *__restrict__ C, int64_t ldc,
-                                                       float alpha, float beta) {
+                                                       const float *__restrict__ B, int64_t yk,
+                                                       int64_t yj, float *__restrict__ C,
+                                                       int64_t ci, int64_t cj, float alpha,
+                                                       float beta) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * 4 + wave) * RW;
 
@@ -49,24 +61,34 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
         if (k + 3 < K) {
 #pragma unroll
             for (int r = 0; r < RW; ++r) a[r] = load16_n(arow[r] + k);
-            if (NR >= 4 && N == NR) {
-                // Whole rows of B: NR/4 16-byte loads per k.
+            if constexpr (YM == 1) {
+                // Whole rows of y: NR/4 16-byte loads per k.
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
                     for (int j4 = 0; j4 < NR / 4; ++j4) {
-                        const f32x4 v = load16_n(B + (int64_t)(k + e) * ldb + 4 * j4);
+                        const f32x4 v = load16_n(B + (int64_t)(k + e) * yk + 4 * j4);
                         b[e][4 * j4 + 0] = v.x;
                         b[e][4 * j4 + 1] = v.y;
                         b[e][4 * j4 + 2] = v.z;
                         b[e][4 * j4 + 3] = v.w;
                     }
+            } else if constexpr (YM == 2) {
+                // Columns of y contiguous along k: one 16-byte load per column.
+#pragma unroll
+                for (int j = 0; j < NR; ++j) {
+                    const f32x4 v = load16_n(B + (int64_t)min(j, N - 1) * yj + k);
+                    b[0][j] = v.x;
+                    b[1][j] = v.y;
+                    b[2][j] = v.z;
+                    b[3][j] = v.w;
+                }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
                     for (int j = 0; j < NR; ++j)
-                        b[e][j] = B[(int64_t)(k + e) * ldb + min(j, N - 1)];
+                        b[e][j] = B[(int64_t)(k + e) * yk + (int64_t)min(j, N - 1) * yj];
             }
         } else {
             // Last partial piece of the row: terms with k >= K are zero.
@@ -81,7 +103,8 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
             for (int e = 0; e < 4; ++e)
 #pragma unroll
                 for (int j = 0; j < NR; ++j)
-                    b[e][j] = k + e < K ? B[(int64_t)(k + e) * ldb + min(j, N - 1)] : 0.0f;
+                    b[e][j] = k + e < K ? B[(int64_t)(k + e) * yk + (int64_t)min(j, N - 1) * yj]
+                                        : 0.0f;
         }
 #pragma unroll
         for (int r = 0; r < RW; ++r)
@@ -109,37 +132,72 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
 #pragma unroll
                 for (int j = 0; j < NR; ++j)
                     if (j < N) {
-                        float *dst = C + (int64_t)(row0 + r) * ldc + j;
+                        float *dst = C + (int64_t)(row0 + r) * ci + (int64_t)j * cj;
                         *dst = epilogue(acc[r][j], alpha, beta, dst);
                     }
     }
 }
 
-template <int NR>
-static hipError_t launch_cols(const Problem &p, hipStream_t s) {
-    // More rows per wave re-use each loaded row of B more often.
+// One streaming product as above: X (rows x K, row stride ldx), y (K x cols,
+// strides yk, yj), out (rows x cols, strides ci, cj).
+struct ColStream {
+    int rows, cols, K;
+    const float *X;
+    int64_t ldx;
+    const float *y;
+    int64_t yk, yj;
+    float *out;
+    int64_t ci, cj;
+    float alpha, beta;
+};
+
+template <int NR, int YM>
+static hipError_t launch_cols(const ColStream &q, hipStream_t s) {
+    // More rows per wave re-use each loaded row of y more often.
     constexpr int RW = NR <= 2 ? 4 : 8;
-    const int64_t groups = (p.M + 4 * RW - 1) / (4 * RW);
+    const int64_t groups = (q.rows + 4 * RW - 1) / (4 * RW);
     if (groups > INT32_MAX) return hipErrorInvalidValue;
-    return launch(skinny_n_kernel<NR, RW>, dim3((unsigned)groups), dim3(256), 0, s, p.M, p.N, p.K,
-                  p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta);
+    return launch(skinny_n_kernel<NR, RW, YM>, dim3((unsigned)groups), dim3(256), 0, s, q.rows,
+                  q.cols, q.K, q.X, q.ldx, q.y, q.yk, q.yj, q.out, q.ci, q.cj, q.alpha, q.beta);
 }
 
-hipError_t launch_skinny_n(const Problem &p, hipStream_t s) {
+template <int NR>
+static hipError_t launch_cols_of(const ColStream &q, hipStream_t s) {
+    if (NR >= 4 && q.cols == NR && q.yj == 1) return launch_cols<NR, 1>(q, s);
+    if (q.yk == 1) return launch_cols<NR, 2>(q, s);
+    return launch_cols<NR, 0>(q, s);
+}
+
+static hipError_t launch_col_stream(const ColStream &p, hipStream_t s) {
     // More than 8 columns: one pass per group of 8 columns.
-    for (int c0 = 0; c0 < p.N; c0 += SKINNY_N_MAX_COLS) {
-        Problem q = p;
-        q.N = p.N - c0 < SKINNY_N_MAX_COLS ? p.N - c0 : SKINNY_N_MAX_COLS;
-        q.B = p.B + c0;
-        q.C = p.C + c0;
+    for (int c0 = 0; c0 < p.cols; c0 += SKINNY_N_MAX_COLS) {
+        ColStream q = p;
+        q.cols = p.cols - c0 < SKINNY_N_MAX_COLS ? p.cols - c0 : SKINNY_N_MAX_COLS;
+        q.y = p.y + (int64_t)c0 * p.yj;
+        q.out = p.out + (int64_t)c0 * p.cj;
         hipError_t e;
-        if (q.N == 1) e = launch_cols<1>(q, s);
-        else if (q.N == 2) e = launch_cols<2>(q, s);
-        else if (q.N <= 4) e = launch_cols<4>(q, s);
-        else e = launch_cols<8>(q, s);
+        if (q.cols == 1) e = launch_cols_of<1>(q, s);
+        else if (q.cols == 2) e = launch_cols_of<2>(q, s);
+        else if (q.cols <= 4) e = launch_cols_of<4>(q, s);
+        else e = launch_cols_of<8>(q, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Few columns of C with A not transposed: X = A, y = op(B), out = C.
+hipError_t launch_skinny_cols(const Problem &p, hipStream_t s) {
+    const ColStream q{p.M, p.N, p.K, p.A, p.lda, p.B, p.tb ? 1 : p.ldb, p.tb ? p.ldb : 1,
+                      p.C, p.ldc, 1, p.alpha, p.beta};
+    return launch_col_stream(q, s);
+}
+
+// Few rows of C with B transposed: C^T = B^T * op(A)^T, so X = the stored N x K
+// array B, y = op(A)^T (K x M), out = C^T.
+hipError_t launch_skinny_rows_tb(const Problem &p, hipStream_t s) {
+    const ColStream q{p.N, p.M, p.K, p.B, p.ldb, p.A, p.ta ? p.lda : 1, p.ta ? 1 : p.lda,
+                      p.C, 1, p.ldc, p.alpha, p.beta};
+    return launch_col_stream(q, s);
 }
 
 }  // namespace sgemm

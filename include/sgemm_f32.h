@@ -57,8 +57,10 @@ extern "C" {
 #define SGEMM_F32_ALGO_LDS_TILED 2     /* 16x16 tiles staged in LDS */
 #define SGEMM_F32_ALGO_VALU_REGBLOCK 3 /* LDS double buffer, 8x8 register tiles, v_fma_f32 */
 #define SGEMM_F32_ALGO_MFMA 4          /* LDS double buffer, fp32 matrix cores */
-#define SGEMM_F32_ALGO_SKINNY 5        /* M <= 8: stream B once, split K in the work-group */
-#define SGEMM_F32_ALGO_SKINNY_N 6      /* N <= 8: stream A once, split K across a wave */
+#define SGEMM_F32_ALGO_SKINNY 5        /* M <= 8: stream op(B) once (B as given: split K in the
+                                          work-group; B transposed: split K across a wave) */
+#define SGEMM_F32_ALGO_SKINNY_N 6      /* N <= 8: stream op(A) once (A as given: split K across
+                                          a wave; A transposed: split K in the work-group) */
 #define SGEMM_F32_ALGO_BF16X6 7        /* bf16 matrix cores, operands split in 3 parts (below) */
 #define SGEMM_F32_ALGO_COUNT 8
 
@@ -136,12 +138,13 @@ const char *sgemm_f32_algo_name(int algo);
  * and A and B may be NULL when alpha == 0 or K == 0.  sgemm_f32() is
  * sgemm_f32_ex(N, N, M, N, K, 1, A, lda, B, ldb, 0, C, ldc), bit for bit.
  *
- * sgemm_f32_ex_algo() forces one rung.  AUTO, NAIVE, LDS_TILED and MFMA accept
- * either storage order; VALU_REGBLOCK, SKINNY and SKINNY_N accept only
- * SGEMM_F32_OP_N for both operands (hipErrorInvalidValue otherwise).  AUTO
- * uses the SKINNY and SKINNY_N rules of sgemm_f32() for untransposed operands
- * and MFMA for every other product; see sgemm_f32_auto_plan() for how AUTO may
- * split an MFMA product into blocks and an edge strip.
+ * sgemm_f32_ex_algo() forces one rung.  AUTO, NAIVE, LDS_TILED, MFMA, SKINNY
+ * and SKINNY_N accept either storage order; VALU_REGBLOCK and BF16X6 accept
+ * only SGEMM_F32_OP_N for both operands (hipErrorInvalidValue otherwise).
+ * AUTO uses the SKINNY and SKINNY_N rules of sgemm_f32() in every storage
+ * order (SKINNY for M <= 8, else SKINNY_N for N <= 8) and MFMA for every other
+ * product; see sgemm_f32_auto_plan() for how AUTO may split an MFMA product
+ * into blocks and an edge strip.
  *
  * sgemm_f32_colmajor() takes the same arguments with every array column-major,
  * as in the reference BLAS sgemm: A is M x K (transa = N, lda >= max(1,M)) or
@@ -247,8 +250,7 @@ hipError_t sgemm_f32_ex_ws(int transa, int transb, int M, int N, int K, float al
  * *n_main receive the extent of C that the chosen algorithm covers; when the
  * algorithm is SGEMM_F32_ALGO_MFMA and N (M) lies 1 to 8 past a multiple of
  * 32, AUTO may leave the last N % 32 columns (M % 32 rows) to a second kernel
- * sized for that strip (the SKINNY_N or SKINNY kernel for untransposed
- * operands, the matrix-core rung otherwise) when the tile cost model says the
+ * sized for that strip (the SKINNY_N or SKINNY kernel) when the tile cost model says the
  * two launches finish sooner: the columns [n_main, N) of all rows, then the
  * rows [m_main, M) of columns [0, n_main).  The blocks of the main part use
  * configuration sgemm_f32_mfma_select(m_main, n_main, K, compute_units).

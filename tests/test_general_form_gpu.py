@@ -17,8 +17,9 @@ pytestmark = pytest.mark.gpu
 
 N_, T_ = sg.OP_N, sg.OP_T
 LAYOUTS = [(N_, N_), (N_, T_), (T_, N_), (T_, T_)]
-TRANS_ALGOS = [sg.ALGO_AUTO, sg.ALGO_NAIVE, sg.ALGO_LDS_TILED, sg.ALGO_MFMA]
-NN_ONLY = [sg.ALGO_VALU_REGBLOCK, sg.ALGO_SKINNY, sg.ALGO_SKINNY_N, sg.ALGO_BF16X6]
+TRANS_ALGOS = [sg.ALGO_AUTO, sg.ALGO_NAIVE, sg.ALGO_LDS_TILED, sg.ALGO_MFMA, sg.ALGO_SKINNY,
+               sg.ALGO_SKINNY_N]
+NN_ONLY = [sg.ALGO_VALU_REGBLOCK, sg.ALGO_BF16X6]
 lid = lambda l: ("T" if l[0] else "N") + ("T" if l[1] else "N")
 name = sg.sgemm_f32_algo_name
 

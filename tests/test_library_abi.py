@@ -176,7 +176,12 @@ def test_auto_plan_splits_edge_strips():
     # the streaming rungs cover the whole product
     assert sg.sgemm_f32_auto_plan(0, 0, 1, 4097, 4096, 256) == (sg.ALGO_SKINNY, 1, 4097)
     assert sg.sgemm_f32_auto_plan(0, 0, 4097, 3, 4096, 256) == (sg.ALGO_SKINNY_N, 4097, 3)
-    assert sg.sgemm_f32_auto_plan(1, 0, 1, 4097, 4096, 256) == (sg.ALGO_MFMA, 1, 4097)
+    # in every storage order
+    for ta in (0, 1):
+        for tb in (0, 1):
+            assert sg.sgemm_f32_auto_plan(ta, tb, 1, 4097, 4096, 256) == (sg.ALGO_SKINNY, 1, 4097)
+            assert sg.sgemm_f32_auto_plan(ta, tb, 4097, 3, 4096, 256) == (sg.ALGO_SKINNY_N, 4097,
+                                                                         3)
     # invalid arguments
     assert sg.sgemm_f32_auto_plan(2, 0, 8, 8, 8, 256)[0] == -1
     assert sg.sgemm_f32_auto_plan(0, 0, -1, 8, 8, 256)[0] == -1
@@ -292,7 +297,7 @@ def test_ex_transposed_ld_rules_accept():
 
 
 def test_ex_untransposed_only_rungs():
-    for algo in (sg.ALGO_VALU_REGBLOCK, sg.ALGO_SKINNY, sg.ALGO_SKINNY_N, sg.ALGO_BF16X6):
+    for algo in (sg.ALGO_VALU_REGBLOCK, sg.ALGO_BF16X6):
         assert _ex(ta=1, lda=8, algo=algo) == INVALID
         assert _ex(tb=1, ldb=8, algo=algo) == INVALID
 
