@@ -151,21 +151,35 @@ struct ColStream {
     float alpha, beta;
 };
 
-template <int NR, int YM>
+template <int NR, int RW, int YM>
 static hipError_t launch_cols(const ColStream &q, hipStream_t s) {
-    // More rows per wave re-use each loaded row of y more often.
-    constexpr int RW = NR <= 2 ? 4 : 8;
     const int64_t groups = (q.rows + 4 * RW - 1) / (4 * RW);
     if (groups > INT32_MAX) return hipErrorInvalidValue;
     return launch(skinny_n_kernel<NR, RW, YM>, dim3((unsigned)groups), dim3(256), 0, s, q.rows,
                   q.cols, q.K, q.X, q.ldx, q.y, q.yk, q.yj, q.out, q.ci, q.cj, q.alpha, q.beta);
 }
 
+// Rows per wave.  More rows re-use each value of y more often; fewer give more
+// work-groups and fewer loads of y per load of X.  Measured on 2048 to 16384
+// rows of 4096 k: two rows when y is read along k (YM 2) and for one column or
+// four whole columns (1.3 to 1.7 times faster than eight rows at 4096 rows); in
+// the other cases (y read value by value, or eight columns) the most rows that
+// still give 256 work-groups.
+template <int NR, int YM>
+static hipError_t launch_cols_rw(const ColStream &q, hipStream_t s) {
+    const bool two = YM == 2 || NR == 1 || (NR == 4 && YM == 1);
+    if (!two && (int64_t)q.rows >= 4 * 8 * 256) return launch_cols<NR, 8, YM>(q, s);
+    if (!two && (int64_t)q.rows >= 4 * 4 * 256) return launch_cols<NR, 4, YM>(q, s);
+    return launch_cols<NR, 2, YM>(q, s);
+}
+
 template <int NR>
 static hipError_t launch_cols_of(const ColStream &q, hipStream_t s) {
-    if (NR >= 4 && q.cols == NR && q.yj == 1) return launch_cols<NR, 1>(q, s);
-    if (q.yk == 1) return launch_cols<NR, 2>(q, s);
-    return launch_cols<NR, 0>(q, s);
+    if constexpr (NR >= 4) {
+        if (q.cols == NR && q.yj == 1) return launch_cols_rw<NR, 1>(q, s);
+    }
+    if (q.yk == 1) return launch_cols_rw<NR, 2>(q, s);
+    return launch_cols_rw<NR, 0>(q, s);
 }
 
 static hipError_t launch_col_stream(const ColStream &p, hipStream_t s) {
