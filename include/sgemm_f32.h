@@ -142,8 +142,8 @@ const char *sgemm_f32_algo_name(int algo);
  * and SKINNY_N accept either storage order; VALU_REGBLOCK and BF16X6 accept
  * only SGEMM_F32_OP_N for both operands (hipErrorInvalidValue otherwise).
  * AUTO uses the SKINNY and SKINNY_N rules of sgemm_f32() in every storage
- * order (SKINNY for M <= 8, else SKINNY_N for N <= 8) and MFMA for every other
- * product; see sgemm_f32_auto_plan() for how AUTO may split an MFMA product
+ * order (SKINNY for M <= 8, else SKINNY_N for N <= 8; with A transposed and B
+ * not, up to 24) and MFMA for every other product; see sgemm_f32_auto_plan() for how AUTO may split an MFMA product
  * into blocks and an edge strip.
  *
  * sgemm_f32_colmajor() takes the same arguments with every array column-major,
