@@ -182,6 +182,15 @@ def test_auto_plan_splits_edge_strips():
             assert sg.sgemm_f32_auto_plan(ta, tb, 1, 4097, 4096, 256) == (sg.ALGO_SKINNY, 1, 4097)
             assert sg.sgemm_f32_auto_plan(ta, tb, 4097, 3, 4096, 256) == (sg.ALGO_SKINNY_N, 4097,
                                                                          3)
+    # with A transposed and B not, up to 24 rows or columns stream; the other orders
+    # take the matrix cores from 9 on
+    for M, N, algo in [(12, 4096, sg.ALGO_SKINNY), (24, 4096, sg.ALGO_SKINNY),
+                       (4096, 16, sg.ALGO_SKINNY_N), (4096, 24, sg.ALGO_SKINNY_N),
+                       (25, 4096, sg.ALGO_MFMA), (4096, 25, sg.ALGO_MFMA)]:
+        assert sg.sgemm_f32_auto_plan(1, 0, M, N, 4096, 256)[0] == algo, (M, N)
+    for ta, tb in [(0, 0), (0, 1), (1, 1)]:
+        assert sg.sgemm_f32_auto_plan(ta, tb, 12, 4096, 4096, 256)[0] == sg.ALGO_MFMA
+        assert sg.sgemm_f32_auto_plan(ta, tb, 4096, 12, 4096, 256)[0] == sg.ALGO_MFMA
     # invalid arguments
     assert sg.sgemm_f32_auto_plan(2, 0, 8, 8, 8, 256)[0] == -1
     assert sg.sgemm_f32_auto_plan(0, 0, -1, 8, 8, 256)[0] == -1
