@@ -34,7 +34,10 @@ __device__ __forceinline__ f32x4 load16_n(const float *p) {
 // X[i][k] = A[i*lda + k], y[k][j] = B[k*yk + j*yj], out[i][j] = C[i*ci + j*cj].
 // YM: how a lane reads its four k of y: 0 one value at a time, 1 whole rows of y
 // as 16-byte loads (yj == 1 and N == NR >= 4), 2 four consecutive k of each
-// column as one 16-byte load (yk == 1).
+// column as one 16-byte load (yk == 1), 3 rows of y as NR values although N <
+// NR (yj == 1, yk + N >= NR): the values past column N - 1 come from the next
+// row or the row padding of y and only feed outputs that are not stored; the
+// last four k rows, where that would read past the matrix, go value by value.
 template <int NR, int RW, int YM>
 __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                                                        const float *__restrict__ A, int64_t lda,
@@ -61,18 +64,26 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
         if (k + 3 < K) {
 #pragma unroll
             for (int r = 0; r < RW; ++r) a[r] = load16_n(arow[r] + k);
-            if constexpr (YM == 1) {
-                // Whole rows of y: NR/4 16-byte loads per k.
+            if constexpr (YM == 1 || YM == 3) {
+                if (YM == 1 || k + 4 < K) {
+                    // Whole rows of y: NR/4 16-byte loads per k.
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                    for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int j4 = 0; j4 < NR / 4; ++j4) {
-                        const f32x4 v = load16_n(B + (int64_t)(k + e) * yk + 4 * j4);
-                        b[e][4 * j4 + 0] = v.x;
-                        b[e][4 * j4 + 1] = v.y;
-                        b[e][4 * j4 + 2] = v.z;
-                        b[e][4 * j4 + 3] = v.w;
-                    }
+                        for (int j4 = 0; j4 < NR / 4; ++j4) {
+                            const f32x4 v = load16_n(B + (int64_t)(k + e) * yk + 4 * j4);
+                            b[e][4 * j4 + 0] = v.x;
+                            b[e][4 * j4 + 1] = v.y;
+                            b[e][4 * j4 + 2] = v.z;
+                            b[e][4 * j4 + 3] = v.w;
+                        }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int j = 0; j < NR; ++j)
+                            b[e][j] = B[(int64_t)(k + e) * yk + min(j, N - 1)];
+                }
             } else if constexpr (YM == 2) {
                 // Columns of y contiguous along k: one 16-byte load per column.
 #pragma unroll
@@ -167,7 +178,7 @@ static hipError_t launch_cols(const ColStream &q, hipStream_t s) {
 // still give 256 work-groups.
 template <int NR, int YM>
 static hipError_t launch_cols_rw(const ColStream &q, hipStream_t s) {
-    const bool two = YM == 2 || NR == 1 || (NR == 4 && YM == 1);
+    const bool two = YM == 2 || NR == 1 || (NR == 4 && (YM == 1 || YM == 3));
     if (!two && (int64_t)q.rows >= 4 * 8 * 256) return launch_cols<NR, 8, YM>(q, s);
     if (!two && (int64_t)q.rows >= 4 * 4 * 256) return launch_cols<NR, 4, YM>(q, s);
     return launch_cols<NR, 2, YM>(q, s);
@@ -177,6 +188,7 @@ template <int NR>
 static hipError_t launch_cols_of(const ColStream &q, hipStream_t s) {
     if constexpr (NR >= 4) {
         if (q.cols == NR && q.yj == 1) return launch_cols_rw<NR, 1>(q, s);
+        if (q.yj == 1 && q.yk != 1 && q.yk + q.cols >= NR) return launch_cols_rw<NR, 3>(q, s);
     }
     if (q.yk == 1) return launch_cols_rw<NR, 2>(q, s);
     return launch_cols_rw<NR, 0>(q, s);

@@ -46,7 +46,7 @@ def _run(As, Bs, M, N, K, ta, tb, alpha, beta, C0, algo=sg.ALGO_AUTO, tile=None,
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lid)
 @pytest.mark.parametrize("algo", TRANS_ALGOS, ids=name)
 @pytest.mark.parametrize("shape", [(37, 29, 53), (130, 67, 129), (300, 517, 259), (20, 130, 90),
-                                   (130, 20, 90)],
+                                   (130, 20, 90), (6, 70, 45), (70, 6, 45)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_layouts_exact_integers(shape, algo, layout):
     M, N, K = shape

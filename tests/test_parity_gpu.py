@@ -259,6 +259,11 @@ def test_few_columns(shape, algo):
     A, B = inputs(M, N, K, "normal", seed=400 + M + N + K, lda=K + 1)
     C = _run(A, B, M, N, K, algo, offset_elems=1)
     check_full(A, B, M, N, K, C, f"{name(algo)} {shape}")
+    # padded rows of B (NaN in the padding): rows of B narrower than the kernel's
+    # vectors are read whole, padding included, which must not reach C
+    A, B = inputs(M, N, K, "normal", seed=500 + M + N + K, ldb=N + 3)
+    C = _run(A, B, M, N, K, algo)
+    check_full(A, B, M, N, K, C, f"{name(algo)} {shape} padded B")
 
 
 # ---------------------------------------------------------------- 64-bit offsets
