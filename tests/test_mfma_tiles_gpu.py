@@ -80,6 +80,7 @@ WIDE = [
     ((0, 0), 64, 48, 40, 2_200_000, 48),        # A k-contiguous, 255 rows apart
     ((0, 0), 64, 48, 16, 40, 36_000_000),       # B n-contiguous, 15 rows apart
     ((1, 1), 64, 48, 16, 36_000_000, 2_200_000),  # both transposed
+    ((0, 0), 64, 48, 40, 18_000_000, 48),       # A k-contiguous, 31 rows apart (32-row blocks)
 ]
 
 
@@ -104,8 +105,9 @@ def test_wide_row_strides(case):
         dev[name] = buf
     stream = torch.cuda.current_stream()
     try:
-        # tile 0 forced, the automatic tile, and (untransposed only) the split rung
-        runs = [0, None] + (["bf16x6"] if (ta, tb) == (0, 0) else [])
+        # every tile forced, the automatic tile, and (untransposed only) the split rung
+        runs = list(range(sg.sgemm_f32_mfma_tiles())) + [None] + \
+            (["bf16x6"] if (ta, tb) == (0, 0) else [])
         for tile in runs:
             C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
             log(f"[gpu] wide strides {'T' if ta else 'N'}{'T' if tb else 'N'} tile={tile} "
