@@ -37,7 +37,9 @@ __device__ __forceinline__ f32x4 load16_n(const float *p) {
 // column as one 16-byte load (yk == 1), 3 rows of y as NR values although N <
 // NR (yj == 1, yk + N >= NR): the values past column N - 1 come from the next
 // row or the row padding of y and only feed outputs that are not stored; the
-// last four k rows, where that would read past the matrix, go value by value.
+// last four k rows, where that would read past the matrix, go value by value;
+// 4 (NR == N == 2, y dense: yk == 2, yj == 1) a lane's four rows are eight
+// consecutive floats, read as two 16-byte loads.
 template <int NR, int RW, int YM>
 __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                                                        const float *__restrict__ A, int64_t lda,
@@ -84,6 +86,17 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                         for (int j = 0; j < NR; ++j)
                             b[e][j] = B[(int64_t)(k + e) * yk + min(j, N - 1)];
                 }
+            } else if constexpr (YM == 4) {
+                const f32x4 v0 = load16_n(B + (int64_t)k * 2);
+                const f32x4 v1 = load16_n(B + (int64_t)k * 2 + 4);
+                b[0][0] = v0.x;
+                b[0][1] = v0.y;
+                b[1][0] = v0.z;
+                b[1][1] = v0.w;
+                b[2][0] = v1.x;
+                b[2][1] = v1.y;
+                b[3][0] = v1.z;
+                b[3][1] = v1.w;
             } else if constexpr (YM == 2) {
                 // Columns of y contiguous along k: one 16-byte load per column.
 #pragma unroll
@@ -178,7 +191,7 @@ static hipError_t launch_cols(const ColStream &q, hipStream_t s) {
 // still give 256 work-groups.
 template <int NR, int YM>
 static hipError_t launch_cols_rw(const ColStream &q, hipStream_t s) {
-    const bool two = YM == 2 || NR == 1 || (NR == 4 && (YM == 1 || YM == 3));
+    const bool two = YM == 2 || YM == 4 || NR == 1 || (NR == 4 && (YM == 1 || YM == 3));
     if (!two && (int64_t)q.rows >= 4 * 8 * 256) return launch_cols<NR, 8, YM>(q, s);
     if (!two && (int64_t)q.rows >= 4 * 4 * 256) return launch_cols<NR, 4, YM>(q, s);
     return launch_cols<NR, 2, YM>(q, s);
@@ -186,6 +199,9 @@ static hipError_t launch_cols_rw(const ColStream &q, hipStream_t s) {
 
 template <int NR>
 static hipError_t launch_cols_of(const ColStream &q, hipStream_t s) {
+    if constexpr (NR == 2) {
+        if (q.cols == 2 && q.yj == 1 && q.yk == 2) return launch_cols_rw<NR, 4>(q, s);
+    }
     if constexpr (NR >= 4) {
         if (q.cols == NR && q.yj == 1) return launch_cols_rw<NR, 1>(q, s);
         if (q.yj == 1 && q.yk != 1 && q.yk + q.cols >= NR) return launch_cols_rw<NR, 3>(q, s);

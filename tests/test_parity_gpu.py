@@ -246,7 +246,7 @@ def test_torch_matmul_helper():
 
 # ---------------------------------------------------------------- few columns
 FEW_COLS = [(4096, 1, 4096), (4095, 3, 1023), (1000, 8, 777), (33, 5, 4099), (4096, 9, 257),
-            (17, 2, 1), (300, 7, 5)]
+            (17, 2, 1), (300, 7, 5), (513, 2, 1031)]
 
 
 @pytest.mark.parametrize("algo", [sg.ALGO_SKINNY_N, sg.ALGO_AUTO], ids=name)
