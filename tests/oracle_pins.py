@@ -286,7 +286,49 @@ def pin_ex_closed_forms(lib):
     assert np.all(C == 0.0)
 
 
+def _padded_store(X, trans, pad):
+    """The stored array of the logical operand X, transposed or not, as a view with
+    ``pad`` NaN floats at the end of every stored row (so ld = row length + pad)."""
+    st = X.T if trans else X
+    r, c = st.shape
+    buf = np.full((r, c + pad), np.nan, dtype=np.float32)
+    buf[:, :c] = st
+    return buf[:, :c]
+
+
+def pin_ex_padded_strides(lib):
+    """Padded leading dimensions in all four layouts and for C_in, against the exact
+    integer result: alpha*sum_k opA[i][k]*opB[k][j] + beta*C_in[i][j] (the definition
+    of page "CUDA算子优化(4)：矩阵乘法", section "矩阵乘法的数学定义", with the BLAS
+    operands).  Every stored row carries NaN padding, and M, N, K and the three
+    paddings all differ, so reading any array with a row length in place of its
+    leading dimension (or a padding element) gives a wrong or non-finite value."""
+    M, N, K = 7, 9, 11
+    X = _gen(M, K, 101, 0, "smallint")      # op(A)
+    Y = _gen(K, N, 101, 1, "smallint")      # op(B)
+    Cin = _gen(M, N, 101, 2, "smallint")
+    alpha, beta = 2, -3
+    xi, yi, ci = X.astype(np.int64), Y.astype(np.int64), Cin.astype(np.int64)
+    exact = (alpha * (xi @ yi) + beta * ci).astype(np.float64)
+    sabs = (abs(alpha) * (np.abs(xi) @ np.abs(yi)) + abs(beta) * np.abs(ci)).astype(np.float64)
+    Cp = _padded_store(Cin, False, 4)
+    assert Cp.strides[0] == 4 * (N + 4)
+    rng = np.random.default_rng(9)
+    r = rng.integers(0, M, 40)
+    c = rng.integers(0, N, 40)
+    for ta in (False, True):
+        for tb in (False, True):
+            A = _padded_store(X, ta, 3)
+            B = _padded_store(Y, tb, 5)
+            C, S = oracle.sgemm_ex(A, B, ta, tb, float(alpha), float(beta), Cp, lib=lib)
+            assert np.array_equal(C, exact), ("padded strides", ta, tb)
+            assert np.array_equal(S, sabs), ("padded strides S", ta, tb)
+            Ce, Se = oracle.sgemm_ex(A, B, ta, tb, float(alpha), float(beta), Cp, rows=r,
+                                     cols=c, lib=lib)
+            assert np.array_equal(Ce, exact[r, c]) and np.array_equal(Se, sabs[r, c]), (ta, tb)
+
+
 ALL_PINS = [pin_all_ones, pin_identity, pin_small_integers, pin_block_identity,
             pin_transpose, pin_brute_force, pin_library_fp64, pin_elements_match_full,
             pin_leading_dimensions, pin_empty_sum, pin_ex_brute_force, pin_ex_library_fp64,
-            pin_ex_plain_form, pin_ex_closed_forms]
+            pin_ex_plain_form, pin_ex_closed_forms, pin_ex_padded_strides]

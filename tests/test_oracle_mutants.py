@@ -41,6 +41,12 @@ MUTANTS = {
     "ex_alpha_dropped": ("double out = p->alpha * c;", "double out = c;"),
     "ex_wrong_sign": ("\n            c += a * b;", "\n            c -= a * b;"),
     "ex_scale_without_abs": ("\n            s += fabs(a) * fabs(b);", "\n            s += a * b;"),
+    # the general form's leading dimensions: a row length read in place of ld
+    "ex_a_uses_k_for_lda": ("(double)p->A[i * p->lda + k]", "(double)p->A[i * p->K + k]"),
+    "ex_at_uses_m_for_lda": ("(double)p->A[k * p->lda + i]", "(double)p->A[k * p->M + i]"),
+    "ex_b_uses_n_for_ldb": ("(double)p->B[k * p->ldb + j]", "(double)p->B[k * p->N + j]"),
+    "ex_bt_uses_k_for_ldb": ("(double)p->B[j * p->ldb + k]", "(double)p->B[j * p->K + k]"),
+    "ex_cin_uses_n_for_ldcin": ("p->Cin[i * p->ldcin + j]", "p->Cin[i * p->N + j]"),
 }
 
 
