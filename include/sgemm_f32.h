@@ -51,7 +51,41 @@
 extern "C" {
 #endif
 
-/* Algorithm ids for sgemm_f32_algo(). */
+/*
+ * Algorithm ids for sgemm_f32_algo(): the rungs of the ladder the pages build,
+ * from one thread per output element up to on-chip tiling, plus the rungs this
+ * library adds for gfx950.  Each computes the same definition; they differ in
+ * how the work is mapped, not in what is computed.
+ *
+ * SGEMM_F32_ALGO_NAIVE: one work-item per element of C, k loop in registers,
+ *   operands read straight from global memory.  The naive kernel of page
+ *   "CUDA内存优化入门：从Naive到Tiled矩阵乘法—Week2学习总结" (§五) and of page
+ *   "CUDA算子优化(4)：矩阵乘法" (section "版本V1朴素矩阵乘法"), with the &&
+ *   bounds guard of the first page.
+ * SGEMM_F32_ALGO_LDS_TILED: 16 x 16 tiles of A and B staged in LDS, one
+ *   element of C per work-item, zero-filled tiles past the edges, one barrier
+ *   after the tile load and one before it is overwritten.  The tiled kernel of
+ *   the first page (§六, with the padded tile of §八 "避免Bank Conflict") and
+ *   of page "CUDA算子优化(4)：矩阵乘法" (section "版本V1共享内存分块"); the
+ *   index map is the one walked through on page "【infra之路】Tiled Matrix
+ *   Multiplication详解".
+ * SGEMM_F32_ALGO_VALU_REGBLOCK: the tiled kernel with an 8 x 8 block of C per
+ *   work-item in registers, two LDS stages and an unrolled k loop of fused
+ *   multiply-adds: the unrolling and fmaf steps of page "GPU programming with
+ *   C++ and CUDA" (chapter 7) and the "optimise register use" and "double
+ *   buffering" items of the first page's checklist (§八).
+ * SGEMM_F32_ALGO_MFMA: the tiled kernel of "版本V1共享内存分块" with the block
+ *   product done on the fp32 matrix cores (v_mfma_f32_32x32x2f32), 16-byte
+ *   loads and an LDS ring: the "Tensor Core", "float4 loads" and "double
+ *   buffering" items of the first page's checklist (§七, §八) on full-precision
+ *   matrix cores.
+ * SGEMM_F32_ALGO_SKINNY / SKINNY_N: products with at most 8 rows (columns) of
+ *   C, whose arithmetic intensity I = MNK / (2(MK+KN+MN)) (page
+ *   "CUDA算子优化(4)：矩阵乘法", section "计算强度") is near 0.5 flop/byte, so
+ *   they are bound by memory bandwidth: the large operand is streamed once.
+ * SGEMM_F32_ALGO_BF16X6: the fp32 product on the bf16 matrix cores (the
+ *   "Tensor Core" step of the first page's §七 and §八), described below.
+ */
 #define SGEMM_F32_ALGO_AUTO 0          /* chosen from the shape */
 #define SGEMM_F32_ALGO_NAIVE 1         /* one thread per element of C */
 #define SGEMM_F32_ALGO_LDS_TILED 2     /* 16x16 tiles staged in LDS */
@@ -81,7 +115,12 @@ hipError_t sgemm_f32(int M, int N, int K,
 
 /*
  * Same operation and contract as sgemm_f32(), forcing one algorithm of the
- * ladder (an SGEMM_F32_ALGO_* id).  Every algorithm accepts every valid
+ * ladder (an SGEMM_F32_ALGO_* id; the rungs and the passages that define them
+ * are listed above: the naive and tiled kernels of page "CUDA内存优化入门：从
+ * Naive到Tiled矩阵乘法—Week2学习总结" §五 and §六 and of page
+ * "CUDA算子优化(4)：矩阵乘法", sections "版本V1朴素矩阵乘法" and
+ * "版本V1共享内存分块", and the unroll and fmaf steps of page "GPU programming
+ * with C++ and CUDA", chapter 7).  Every algorithm accepts every valid
  * shape; SGEMM_F32_ALGO_SKINNY with M > 8 processes the rows in groups of 8,
  * SGEMM_F32_ALGO_SKINNY_N with N > 8 the columns in groups of 8.
  */
