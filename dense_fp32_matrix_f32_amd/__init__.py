@@ -22,6 +22,28 @@ __all__ = ["matmul", "sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f
            "OP_N", "OP_T"]
 
 
+def _layout(rows, cols, s0, s1, name):
+    """(leading dimension, transposed) of a rows x cols view with element strides
+    (s0, s1): row-major when its column stride is 1, the transpose of a row-major
+    array when its row stride is 1.  A stride shorter than the row it steps over
+    (a broadcast or overlapping view, e.g. ``expand``) is rejected: the library
+    would read or write past the view's memory with the leading dimension it
+    implies."""
+    if rows == 0 or cols == 0:
+        return max(cols, 1), False
+    if cols == 1 or s1 == 1:
+        if rows > 1 and s0 < cols:
+            raise ValueError(f"{name}: row stride {s0} is shorter than a row ({cols}); "
+                             "broadcast or overlapping views are not supported")
+        return (s0 if rows > 1 else cols), False
+    if rows == 1 or s0 == 1:
+        if s1 < rows:
+            raise ValueError(f"{name}: column stride {s1} is shorter than a column ({rows}); "
+                             "broadcast or overlapping views are not supported")
+        return s1, True
+    raise ValueError(f"{name} needs a unit stride in one dimension")
+
+
 def _operand(t, name):
     """(pointer, leading dimension, transposed) of a 2-D float32 CUDA tensor that is
     row-major (unit column stride) or the transpose of a row-major array (unit row
@@ -32,13 +54,8 @@ def _operand(t, name):
     if t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU")
     rows, cols = t.shape
-    if t.numel() == 0 or cols <= 1 or t.stride(1) == 1:
-        ld = t.stride(0) if rows > 1 else cols
-        return t.data_ptr(), max(ld, cols, 1), False
-    if rows <= 1 or t.stride(0) == 1:
-        ld = t.stride(1)
-        return t.data_ptr(), max(ld, rows, 1), True
-    raise ValueError(f"{name} needs a unit stride in one dimension")
+    ld, trans = _layout(rows, cols, t.stride(0), t.stride(1), name)
+    return t.data_ptr(), ld, trans
 
 
 def matmul(A, B, out=None, algo="auto", stream=None, alpha=1.0, beta=0.0, workspace=None):
