@@ -143,9 +143,8 @@ constexpr int NAIVE_X = 64, NAIVE_Y = 4;
 __global__ __launch_bounds__(NAIVE_X *NAIVE_Y) void naive_kernel(
     int M, int N, int K, const float *__restrict__ A, const float *__restrict__ B, Strides st,
     float *__restrict__ C, int64_t ldc, float alpha, float beta, int tiles_n) {
-    const int bn = blockIdx.x % tiles_n, bm = blockIdx.x / tiles_n;
-    const int col = bn * NAIVE_X + threadIdx.x;
-    const int row = bm * NAIVE_Y + threadIdx.y;
+    int row, col;
+    element_of(blockIdx.x, tiles_n, NAIVE_Y, NAIVE_X, threadIdx.x, threadIdx.y, &row, &col);
     if (row >= M || col >= N) return;
     const float *a = A + (int64_t)row * st.ai;
     const float *b = B + (int64_t)col * st.bj;
@@ -180,8 +179,8 @@ __global__ __launch_bounds__(TILE *TILE) void lds_tiled_kernel(
     __shared__ float As[TILE][TILE + 1];
     __shared__ float Bs[TILE][TILE + 1];
     const int tx = threadIdx.x, ty = threadIdx.y;
-    const int bn = blockIdx.x % tiles_n, bm = blockIdx.x / tiles_n;
-    const int row = bm * TILE + ty, col = bn * TILE + tx;
+    int row, col;
+    element_of(blockIdx.x, tiles_n, TILE, TILE, tx, ty, &row, &col);
     float sum = 0.0f;
     for (int k0 = 0; k0 < K; k0 += TILE) {
         const int ka = k0 + tx, kb = k0 + ty;

@@ -41,4 +41,19 @@ SGEMM_HD inline void tile_order(int pid, int tiles_m, int tiles_n, int group_m, 
     group_tile(xcd_remap(pid, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
 }
 
+// The element of C owned by work-item (tx, ty) of work-group `block` in the
+// rungs that compute one element per work-item (naive and LDS-tiled).  The
+// work-groups cover C with tile_m x tile_n tiles numbered row by row, tiles_n
+// to a tile row, so the 1-D id stands for the 2-D block (x = block % tiles_n,
+// y = block / tiles_n); then, as in the tiled kernels of the pages, the row is
+// y * tile_m + ty and the column x * tile_n + tx (page "【infra之路】Tiled
+// Matrix Multiplication详解", the walk-through of the index computation: with
+// a tile of 4, block (1, 2) and thread (3, 1) own row 9, column 7).
+SGEMM_HD inline void element_of(int block, int tiles_n, int tile_m, int tile_n, int tx, int ty,
+                                int *row, int *col) {
+    const int bx = block % tiles_n, by = block / tiles_n;
+    *row = by * tile_m + ty;
+    *col = bx * tile_n + tx;
+}
+
 }  // namespace sgemm

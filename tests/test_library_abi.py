@@ -12,6 +12,7 @@ import pytest
 
 import dense_fp32_matrix_f32_amd as sg
 from dense_fp32_matrix_f32_amd import _binding
+from oracle_pins import read_golden
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 INVALID = _binding.HIP_ERROR_INVALID_VALUE
@@ -121,6 +122,34 @@ def test_tile_order_is_a_bijection(tmp_path):
     shapes += [32, 33, 8, 64, 32, 8, 16, 16, 8]   # the ragged and 8192^3 grids
     out = subprocess.run([str(exe), *map(str, shapes)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout[-2000:]
+
+
+def test_element_index_matches_the_tiled_walkthrough(tmp_path):
+    """The one-element-per-work-item rungs (naive, LDS-tiled) number their work-groups
+    in one dimension; their index map must give the element of the worked example
+    on page "【infra之路】Tiled Matrix Multiplication详解" (tile 4, block (1, 2),
+    thread (3, 1) -> C[9][7]) for any width of the tile grid, and cover every
+    element of C once on ragged shapes with the rungs' own tile sizes."""
+    exe = tmp_path / "element_index_check"
+    subprocess.check_call(["g++", "-O1", "-std=c++17",
+                           "-I", os.path.join(ROOT, "dense_fp32_matrix_f32_amd", "csrc"),
+                           os.path.join(ROOT, "tests", "host", "element_index_check.cpp"),
+                           "-o", str(exe)])
+    g = read_golden("tiled_block_example.txt")
+    t = int(g["index_tile"])
+    bx, by = int(g["index_block_x"]), int(g["index_block_y"])
+    tx, ty = int(g["index_thread_x"]), int(g["index_thread_y"])
+    want = (int(g["index_row"]), int(g["index_col"]))
+    for tiles_n in (bx + 1, 3, 4, 7, 1000):
+        block = by * tiles_n + bx
+        out = subprocess.run([str(exe), "at", str(block), str(tiles_n), str(t), str(t), str(tx),
+                              str(ty)], capture_output=True, text=True, check=True).stdout
+        assert tuple(map(int, out.split())) == want, (tiles_n, out)
+    # the rungs' own tiles: 16 x 16 (LDS-tiled), 4 rows x 64 columns (naive)
+    for M, N in [(1, 1), (9, 7), (16, 16), (17, 65), (300, 517), (4095, 63)]:
+        for tm, tn in [(16, 16), (4, 64), (t, t)]:
+            subprocess.run([str(exe), "cover", str(M), str(N), str(tm), str(tn)], check=True,
+                           capture_output=True)
 
 
 def test_mfma_tile_table():
