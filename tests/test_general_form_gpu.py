@@ -138,6 +138,23 @@ def test_product_free_cases(layout):
     assert np.array_equal(C, -C0)
 
 
+@pytest.mark.parametrize("algo", [sg.ALGO_AUTO, sg.ALGO_SKINNY], ids=name)
+@pytest.mark.parametrize("shape", [(2, 4096, 4096), (2, 1000, 1023), (2, 37, 4093), (2, 515, 6)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_two_rows_both_transposed(shape, algo):
+    """Two rows of C with both operands transposed and stored dense: the few-rows
+    product runs as the few-columns kernel on C^T = B^T A^T, whose right operand
+    (A as stored, K x 2 with lda = 2) has rows of two values; K % 4 != 0 leaves a
+    tail of k rows after the whole vectors."""
+    M, N, K = shape
+    As, Bs, C0 = _operands(M, N, K, "smallint", 800 + N + K, T_, T_)
+    assert As.shape == (K, 2) and Bs.shape == (N, K)
+    for alpha, beta in [(1.0, 0.0), (2.0, -3.0)]:
+        C = _run(As, Bs, M, N, K, T_, T_, alpha, beta, C0, algo)
+        check_ex(As, Bs, M, N, K, T_, T_, alpha, beta, C0, C,
+                 f"{name(algo)} TT {M}x{N}x{K} a={alpha} b={beta}", exact=True)
+
+
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lid)
 def test_ragged_large_sampled(layout):
     """The ragged 4095 x 4097 x 1023 workload in every storage order, on sampled rows,

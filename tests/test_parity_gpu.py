@@ -108,7 +108,7 @@ def test_identity_b_1024(algo):
 
 
 # ---------------------------------------------------------------- 2048 x 3072 x 4096
-@pytest.mark.parametrize("algo", FAST + [sg.ALGO_LDS_TILED], ids=name)
+@pytest.mark.parametrize("algo", FAST + [sg.ALGO_NAIVE, sg.ALGO_LDS_TILED], ids=name)
 def test_2048x3072x4096(algo):
     M, N, K = 2048, 3072, 4096
     A, B = inputs(M, N, K, "normal", seed=3)
@@ -141,10 +141,17 @@ def test_row_times_matrix_1x4096x4096(algo):
 
 
 # ---------------------------------------------------------------- 8192^3
-@pytest.mark.parametrize("algo", [sg.ALGO_AUTO, sg.ALGO_VALU_REGBLOCK, sg.ALGO_BF16X6], ids=name)
+@functools.lru_cache(maxsize=1)
+def _inputs_8192():
+    n = 8192
+    return inputs(n, n, n, "normal", seed=6)
+
+
+@pytest.mark.parametrize("algo", [sg.ALGO_AUTO, sg.ALGO_VALU_REGBLOCK, sg.ALGO_BF16X6,
+                                  sg.ALGO_NAIVE, sg.ALGO_LDS_TILED], ids=name)
 def test_8192_cubed(algo):
     n = 8192
-    A, B = inputs(n, n, n, "normal", seed=6)
+    A, B = _inputs_8192()
     C = _run(A, B, n, n, n, algo)
     check_sampled(A, B, n, n, n, C, f"{name(algo)} 8192^3", seed=6)
 
@@ -242,6 +249,26 @@ def test_torch_matmul_helper():
     torch.cuda.synchronize()
     check_full(np.ascontiguousarray(A[:, :100]), np.ascontiguousarray(B[:100]), 333, 444, 100,
                C2.cpu().numpy(), "view")
+
+
+def test_torch_matmul_rejects_broadcast_views():
+    """Expanded (stride-0) or overlapping views have no leading dimension the library
+    could use; the helper raises before any launch and leaves out untouched."""
+    torch = torch_cuda()
+    M, N, K = 64, 48, 32
+    row_a = torch.ones(1, K, device="cuda")
+    row_b = torch.ones(1, N, device="cuda")
+    A = torch.ones(M, K, device="cuda")
+    B = torch.ones(K, N, device="cuda")
+    out = torch.full((M, N), 5.0, device="cuda")
+    for a, b, o in [(row_a.expand(M, K), B, out), (A, row_b.expand(K, N), out),
+                    (A, B, torch.full((1, N), 5.0, device="cuda").expand(M, N)),
+                    (A, torch.ones(K, 1, device="cuda").expand(K, N), out),
+                    (A.as_strided((M, K), (K // 2, 1)), B, out)]:
+        with pytest.raises(ValueError):
+            sg.matmul(a, b, out=o)
+    torch.cuda.synchronize()
+    assert torch.all(out == 5.0)
 
 
 # ---------------------------------------------------------------- few columns
