@@ -26,6 +26,8 @@ if ROOT not in sys.path:
 
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (matrix and vector), 2.4 GHz
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix cores
+SPLIT_PART_PRODUCTS = 6       # bf16 part products per fp32 product on the split-precision rung
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_mfma_8192_traffic.txt")
 KERNEL_SOURCES = ["dense_fp32_matrix_f32_amd/csrc/mfma_kernel.h",
                   "dense_fp32_matrix_f32_amd/csrc/mfma_nn.hip",
@@ -93,6 +95,17 @@ def read_traffic():
         return None
 
 
+def split_record(flops: int, ms: float) -> dict:
+    """Throughput of the split-precision rung: the fp32 product's 2MNK flops per second,
+    and the bf16 matrix-core work it issues (six part products, 6 * 2MNK flops) as a
+    fraction of the bf16 matrix peak, the roofline of the units it runs on."""
+    fp32_eq = flops / (ms * 1e-3) / 1e12
+    bf16 = SPLIT_PART_PRODUCTS * fp32_eq
+    return {"kernel_ms": round(ms, 5), "fp32_equivalent_tflops": round(fp32_eq, 3),
+            "bf16_mfma_tflops": round(bf16, 2), "peak_bf16_tflops": PEAK_BF16_TFLOPS,
+            "pct_bf16_peak": round(100 * bf16 / PEAK_BF16_TFLOPS, 2)}
+
+
 def host_threads() -> int:
     try:
         return max(1, len(os.sched_getaffinity(0)))
@@ -114,10 +127,11 @@ def make_inputs(torch, M, N, K, seed, dist="normal", layout=(0, 0)):
 
 
 def time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warmup, layout=(0, 0),
-                 workspace=None):
+                 workspace=None, sclk_log=None):
     """Warm-up, then `steps` timed launches: wall clock between two full
     synchronisations, and per-launch HIP events on the launch stream.  With a
-    workspace tensor, the product goes through sgemm_f32_ex_ws."""
+    workspace tensor, the product goes through sgemm_f32_ex_ws.  With a list as
+    sclk_log, the shader clock read while the timed launches run is appended."""
     stream = torch.cuda.current_stream()
     ta, tb = layout
     lda, ldb, ldc = (M if ta else K), (K if tb else N), N
@@ -146,8 +160,12 @@ def time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warmup, layout=(0,
         starts[i].record(stream)
         call()
         ends[i].record(stream)
+    # read while the queued launches run (host enqueueing is far shorter than them)
+    sclk = gpu_sclk(torch) if sclk_log is not None else None
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if sclk_log is not None:
+        sclk_log.append(sclk)
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return wall, kernel_ms
 
@@ -327,11 +345,7 @@ def config_report(torch, sg, args):
             sms = timed_launches(torch, stream, lambda: _check(sg.sgemm_f32_algo(
                 M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, stream.cuda_stream,
                 sg.ALGO_BF16X6), sg))
-            smed = statistics.median(sms)
-            rec["bf16x6"] = {"kernel_ms_median": round(smed, 5),
-                             "tflops": round(flops / (smed * 1e-3) / 1e12, 3),
-                             "pct_fp32_peak": round(100 * flops / (smed * 1e-3) / 1e12 /
-                                                    PEAK_FP32_TFLOPS, 2)}
+            rec["bf16x6"] = split_record(flops, statistics.median(sms))
         if args.cpu_seconds > 0:
             rec["host_blocked"] = cpu_blocked(A, B, M, N, K, reps=3 if M * N * K < 1e10 else 1)
         if name in ("c1", "c2") and args.cpu_seconds > 0:
@@ -484,8 +498,11 @@ def main(argv=None):
         ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device="cuda")
         print(f"[bench] workspace {nbytes} bytes (sgemm_f32_ex_ws)", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    sclk_before = gpu_sclk(torch)
+    sclk_timed = []
     wall, kms = time_product(torch, sg, M, N, K, dA, dB, dC, algo, args.steps, args.warmup,
-                             layout, workspace=ws)
+                             layout, workspace=ws, sclk_log=sclk_timed)
+    sclk_after = gpu_sclk(torch)
     flops = algorithmic_flops(M, N, K)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (wall / args.steps) / 1e12
@@ -519,6 +536,8 @@ def main(argv=None):
                      "kernel_ms_avg": round(kavg, 4), "kernel_ms_min": round(min(kms), 4),
                      "algorithmic_flops": flops, "algorithmic_bytes": algorithmic_bytes(M, N, K),
                      "intensity_flop_per_byte": round(intensity(M, N, K), 2)},
+        "sclk": {"before": sclk_before, "during_timed": sclk_timed[0] if sclk_timed else None,
+                 "after": sclk_after},
     }
     if used in (sg.ALGO_SKINNY, sg.ALGO_SKINNY_N):
         # few rows or columns: the product streams one operand, so HBM bounds it
@@ -530,13 +549,9 @@ def main(argv=None):
         # matrix cores), reported beside the fp32 result, never as the value
         _, sms = time_product(torch, sg, M, N, K, dA, dB, dC, sg.ALGO_BF16X6, args.steps,
                               args.warmup)
-        savg = sum(sms) / len(sms)
-        rec["bf16x6"] = {"kernel_ms_avg": round(savg, 4),
-                         "kernel_tflops": round(flops / (savg * 1e-3) / 1e12, 3),
-                         "pct_fp32_peak": round(100 * flops / (savg * 1e-3) / 1e12 /
-                                                PEAK_FP32_TFLOPS, 2),
-                         "note": "fp32 product on bf16 matrix cores, operands split into "
-                                 "three bf16 parts (six part products), fp32 accumulation"}
+        rec["bf16x6"] = split_record(flops, sum(sms) / len(sms))
+        rec["bf16x6"]["note"] = ("fp32 product on bf16 matrix cores, operands split into three "
+                                 "bf16 parts (six part products), fp32 accumulation")
     del dA, dB, dC
     if not args.no_also:
         m2, n2, k2 = 2048, 3072, 4096
