@@ -13,12 +13,14 @@ from ._binding import (ALGO_AUTO, ALGO_BF16X6, ALGO_COUNT, ALGO_LDS_TILED, ALGO_
                        sgemm_f32_colmajor, sgemm_f32_ex, sgemm_f32_ex_algo,
                        sgemm_f32_ex_mfma_tile, sgemm_f32_mfma_select, sgemm_f32_mfma_tile,
                        sgemm_f32_mfma_tile_name, sgemm_f32_mfma_tiles, sgemm_f32_select,
-                       sgemm_f32_auto_plan, sgemm_f32_ex_ws, sgemm_f32_workspace_size)
+                       sgemm_f32_auto_plan, sgemm_f32_ex_ws, sgemm_f32_workspace_size,
+                       sgemm_f32_ex_noalloc, SCRATCH_BYTES)
 
 __all__ = ["matmul", "sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_name",
            "sgemm_f32_ex", "sgemm_f32_ex_algo", "sgemm_f32_colmajor", "sgemm_f32_mfma_tiles",
            "sgemm_f32_mfma_tile_name", "sgemm_f32_mfma_select", "sgemm_f32_mfma_tile",
-           "sgemm_f32_ex_mfma_tile", "sgemm_f32_auto_plan", "sgemm_f32_workspace_size", "sgemm_f32_ex_ws", "SgemmError", "ALGOS", "LIB_PATH", "EXPORTED", "lib",
+           "sgemm_f32_ex_mfma_tile", "sgemm_f32_auto_plan", "sgemm_f32_workspace_size", "sgemm_f32_ex_ws",
+           "sgemm_f32_ex_noalloc", "SCRATCH_BYTES", "SgemmError", "ALGOS", "LIB_PATH", "EXPORTED", "lib",
            "OP_N", "OP_T"]
 
 

@@ -35,7 +35,9 @@ EXPORTED = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_select", "sgemm_f32_algo_n
             "sgemm_f32_ex", "sgemm_f32_ex_algo", "sgemm_f32_colmajor",
             "sgemm_f32_mfma_tiles", "sgemm_f32_mfma_tile_name", "sgemm_f32_mfma_select",
             "sgemm_f32_mfma_tile", "sgemm_f32_ex_mfma_tile", "sgemm_f32_auto_plan",
-            "sgemm_f32_workspace_size", "sgemm_f32_ex_ws")
+            "sgemm_f32_workspace_size", "sgemm_f32_ex_ws", "sgemm_f32_ex_noalloc")
+
+SCRATCH_BYTES = 32 << 20   # SGEMM_F32_SCRATCH_BYTES
 
 _lib = None
 
@@ -94,6 +96,8 @@ def lib() -> ctypes.CDLL:
         l.sgemm_f32_ex_ws.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp, ctypes.c_size_t,
                                       vp]
         l.sgemm_f32_ex_ws.restype = i
+        l.sgemm_f32_ex_noalloc.argtypes = ex_args
+        l.sgemm_f32_ex_noalloc.restype = i
         ip = ctypes.POINTER(i)
         l.sgemm_f32_auto_plan.argtypes = [i, i, i, i, i, i, ip, ip]
         l.sgemm_f32_auto_plan.restype = i
@@ -156,6 +160,14 @@ def sgemm_f32_ex_ws(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc
     """sgemm_f32_ex with a device workspace (split-k when it pays); returns the hipError_t."""
     return lib().sgemm_f32_ex_ws(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                  workspace, workspace_bytes, stream)
+
+
+def sgemm_f32_ex_noalloc(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         stream=0) -> int:
+    """sgemm_f32_ex_ws with the library's own device scratch array as the workspace
+    (allocates nothing); returns the hipError_t."""
+    return lib().sgemm_f32_ex_noalloc(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                      ldc, stream)
 
 
 def sgemm_f32_mfma_tile(M, N, K, A, lda, B, ldb, C, ldc, stream=0, tile=0) -> int:

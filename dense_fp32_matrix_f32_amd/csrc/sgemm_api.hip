@@ -2,6 +2,9 @@
 // host (before any HIP call), choice of kernel, and launch on the caller's stream.
 #include "sgemm_f32.h"
 
+#include <atomic>
+#include <mutex>
+
 #include "internal.h"
 
 using sgemm::Problem;
@@ -210,6 +213,48 @@ WsPlan plan_workspace(const Problem &p, int algo, int cus) {
     return best_us < 0.9 * whole ? best : none;
 }
 
+// The two kernels of a split product: partial planes to `planes`, then the
+// fixed-order reduction into C.
+hipError_t launch_split_planes(const Problem &p, const WsPlan &w, float *planes,
+                               hipStream_t stream) {
+    const hipError_t st = sgemm::launch_mfma_splitk(p, stream, w.tile, w.slices, planes);
+    if (st != hipSuccess) return st;
+    return sgemm::launch_splitk_reduce(p, w.slices, planes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Split-k for callers that cannot allocate: the planes go to a file-scope device
+// array of SGEMM_F32_SCRATCH_BYTES.  Each GPU the library runs on holds its own
+// copy, at its own address, until the process ends.  On the host the array's
+// name is not a device address, so its address on each device is looked up once
+// (with that device current) and kept; kernels only ever see that address.
+static __device__ __align__(256) float scratch[SGEMM_F32_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_addr[kMaxDevices];
+std::mutex scratch_lookup;
+
+// Address of the current device's copy of `scratch`.
+hipError_t scratch_on_current_device(float **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *ptr = scratch_addr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> hold(scratch_lookup);
+        ptr = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (ptr == nullptr) return hipErrorInvalidSymbol;
+            scratch_addr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = (float *)ptr;
+    return hipSuccess;
+}
+
 bool handles_transposes(int algo) {
     return algo == SGEMM_F32_ALGO_AUTO || algo == SGEMM_F32_ALGO_NAIVE ||
            algo == SGEMM_F32_ALGO_LDS_TILED || algo == SGEMM_F32_ALGO_MFMA ||
@@ -344,10 +389,26 @@ extern "C" hipError_t sgemm_f32_ex_ws(int transa, int transb, int M, int N, int 
     const Extent a = transa ? extent(A, K, M, lda) : extent(A, M, K, lda);
     const Extent b = transb ? extent(B, N, K, ldb) : extent(B, K, N, ldb);
     if (overlaps(ws, a) || overlaps(ws, b) || overlaps(ws, c)) return hipErrorInvalidValue;
-    float *planes = (float *)workspace;
-    st = sgemm::launch_mfma_splitk(p, stream, w.tile, w.slices, planes);
+    return launch_split_planes(p, w, (float *)workspace, stream);
+}
+
+extern "C" hipError_t sgemm_f32_ex_noalloc(int transa, int transb, int M, int N, int K,
+                                           float alpha, const float *A, int lda, const float *B,
+                                           int ldb, float beta, float *C, int ldc,
+                                           hipStream_t stream) {
+    hipError_t st;
+    if (trivial(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, &st))
+        return st;
+    const Problem p = problem(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    const WsPlan w = plan_workspace(p, choose(transa, transb, M, N, K), sgemm::compute_units());
+    if (w.kind == WS_NONE)
+        return sgemm_f32_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    if ((uint64_t)ws_bytes(w, p) > SGEMM_F32_SCRATCH_BYTES) return hipErrorInvalidValue;
+    float *planes = nullptr;
+    st = scratch_on_current_device(&planes);
     if (st != hipSuccess) return st;
-    return sgemm::launch_splitk_reduce(p, w.slices, planes, stream);
+    // the scratch array is the library's own, so it cannot overlap A, B or C
+    return launch_split_planes(p, w, planes, stream);
 }
 
 extern "C" hipError_t sgemm_f32_ex(int transa, int transb, int M, int N, int K, float alpha,

@@ -23,8 +23,10 @@
  * Ownership.  The caller owns every buffer.  A, B and C are device pointers
  * (hipMalloc, torch or any other device allocation) that must stay valid
  * until the enqueued work completes.  The library allocates nothing, keeps
- * no pointer after returning, and holds no mutable global state; calls may
- * come from several host threads.
+ * no pointer after returning, and holds no mutable global state other than
+ * the per-device address of the scratch array of sgemm_f32_ex_noalloc()
+ * (looked up once per device, under a lock); calls may come from several
+ * host threads.
  *
  * Asynchrony.  Each call validates its arguments on the host, enqueues its
  * kernels on `stream` (0 is the null stream) and returns without waiting.
@@ -280,6 +282,37 @@ hipError_t sgemm_f32_ex_ws(int transa, int transb, int M, int N, int K, float al
                            float *C, int ldc,
                            void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (work recorded under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sgemm_f32_ex_noalloc() is sgemm_f32_ex_ws() with the workspace taken from a
+ * device array inside the library instead of from the caller.
+ *
+ * The array is SGEMM_F32_SCRATCH_BYTES (32 MiB) of device memory, one copy per
+ * GPU the library runs on, held until the process ends; its address on a device
+ * is looked up on the first call made with that device current.  The call
+ * allocates nothing and calls no allocating routine.  When the split planner
+ * (the same as for sgemm_f32_ex_ws()) wants no split, the call is
+ * sgemm_f32_ex(); when it wants one whose planes fit in the array, the planes go
+ * there and the result is bit for bit that of sgemm_f32_ex_ws() with a large
+ * enough workspace; when the planes would need more than
+ * SGEMM_F32_SCRATCH_BYTES (sgemm_f32_workspace_size() tells beforehand), the
+ * call returns hipErrorInvalidValue and enqueues nothing.
+ *
+ * Every call on one GPU shares that GPU's array, and each call overwrites the
+ * part it uses (no part needs to start at zero), so calls whose work overlaps
+ * in time on one GPU (on different streams, or from several host threads)
+ * race and give wrong results: order them on one stream or with events.  Other
+ * arguments, errors and asynchrony are as for sgemm_f32_ex().
+ */
+#define SGEMM_F32_SCRATCH_BYTES (32u << 20)
+
+hipError_t sgemm_f32_ex_noalloc(int transa, int transb, int M, int N, int K, float alpha,
+                                const float *A, int lda,
+                                const float *B, int ldb, float beta,
+                                float *C, int ldc,
+                                hipStream_t stream);
 
 /*
  * How SGEMM_F32_ALGO_AUTO runs an M x N x K product with the given storage

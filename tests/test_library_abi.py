@@ -271,6 +271,26 @@ def test_workspace_size_and_validation():
         == INVALID
 
 
+def test_noalloc_scratch_limit_and_validation():
+    """sgemm_f32_ex_noalloc takes its split planes from a device array of
+    SGEMM_F32_SCRATCH_BYTES; a product whose plan needs more is refused before any
+    launch (host-only here: nothing is dereferenced), and argument errors come first."""
+    hdr = open(os.path.join(ROOT, "include", "sgemm_f32.h"), encoding="utf-8").read()
+    m = re.search(r"#define SGEMM_F32_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == sg.SCRATCH_BYTES == 32 << 20
+    a, b, c = 1 << 40, 1 << 41, 1 << 42
+    M, N, K = 768, 768, 65536
+    assert sg.sgemm_f32_workspace_size(0, 0, M, N, K) > sg.SCRATCH_BYTES
+    assert sg.sgemm_f32_ex_noalloc(0, 0, M, N, K, 1.0, a, K, b, N, 0.0, c, N, 0) == INVALID
+    assert sg.sgemm_f32_ex_noalloc(1, 1, M, N, K, 1.0, a, M, b, K, 0.5, c, N, 0) == INVALID
+    M, N, K = 128, 128, 65536
+    assert 0 < sg.sgemm_f32_workspace_size(0, 0, M, N, K) <= sg.SCRATCH_BYTES
+    assert sg.sgemm_f32_ex_noalloc(0, 0, M, N, K, 1.0, a, K - 1, b, N, 0.0, c, N, 0) == INVALID
+    assert sg.sgemm_f32_ex_noalloc(0, 0, M, N, K, 1.0, a, K, b, N, 0.0, a + 64, N, 0) == INVALID
+    assert sg.sgemm_f32_ex_noalloc(2, 0, M, N, K, 1.0, a, K, b, N, 0.0, c, N, 0) == INVALID
+    assert sg.sgemm_f32_ex_noalloc(0, 0, 0, N, K, 1.0, a, K, b, N, 0.0, c, N, 0) == 0
+
+
 def test_mfma_tile_entry_validates():
     n = sg.sgemm_f32_mfma_tiles()
     for tile in (-1, n):
