@@ -234,6 +234,25 @@ struct Operand {
         return (TOTAL % T::THREADS == 0) || tid + v * T::THREADS < TOTAL;
     }
 
+    // Vector c of the window -> its row and its vector q within the row.  A
+    // k-contiguous window of four vectors per row (16-wide k windows, rows padded
+    // to 20 floats) hands the 16 rows of each 64-vector chunk out so that every 16
+    // consecutive work-items store rows r, r+4, r+8 and r+12: at a pitch of 20
+    // floats those rows start 16 banks apart and together fill the 64 banks once,
+    // where rows r..r+3 would wrap onto the same banks (a two-way conflict on the
+    // 16-byte LDS stores).  Each work-item still loads a whole 16-byte vector and
+    // each wave the same 64-byte row pieces.
+    __device__ __forceinline__ static void place(int c, int &row, int &q) {
+        if constexpr (KC && Q == 4 && TOTAL % 64 == 0 && T::BK + T::PAD_A == 20) {
+            const int l = c & 63;
+            row = (c >> 6) * 16 + ((l >> 2) & 3) * 4 + (l >> 4);
+            q = l & 3;
+        } else {
+            row = c / Q;
+            q = c % Q;
+        }
+    }
+
     // origin: first row (KC) or column of the block; extent: M or N; ld: row
     // stride of the stored array; base/pitch: LDS placement of the window.
     __device__ __forceinline__ void init(const float *X, int64_t ld, int origin, int extent,
@@ -241,7 +260,8 @@ struct Operand {
 #pragma unroll
         for (int v = 0; v < VECS; ++v) {
             const int c = min(tid + v * T::THREADS, TOTAL - 1);
-            const int row = c / Q, q = c % Q;
+            int row, q;
+            place(c, row, q);
             if constexpr (KC) {
                 const int gr = min(origin + row, extent - 1);
                 src[v] = X + (int64_t)gr * ld + q * 4;
