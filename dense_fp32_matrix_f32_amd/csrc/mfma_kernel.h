@@ -108,6 +108,23 @@ __device__ __forceinline__ f32x4 load16_at(const char *base, uint32_t off) {
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// 12-byte loads into the first three lanes of a vector whose fourth is zero:
+// from a 4-byte aligned address, and through a buffer resource as load16_at.
+__device__ __forceinline__ f32x4 load12(const float *p) {
+    f32x4 v;
+    __builtin_memcpy(&v, p, 12);
+    v.w = 0.0f;
+    return v;
+}
+
+__device__ __forceinline__ f32x4 load12_at(const char *base, uint32_t off) {
+    typedef float f32x3 __attribute__((ext_vector_type(3)));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, -1, 0x00020000);
+    const f32x3 x = __builtin_bit_cast(f32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0));
+    return f32x4{x.x, x.y, x.z, 0.0f};
+}
+
 // Scheduling hint for one basic block holding MF MFMAs, DSR LDS reads, DSW LDS
 // writes and VMR global loads: each memory instruction is placed right after an
 // MFMA, so a single wave keeps its matrix core fed while it issues them.  When
@@ -153,13 +170,8 @@ struct MfmaTile {
     static constexpr int TM = WM / 32, TN = WN / 32;     // 32x32 accumulators per wave
     static constexpr int ACC = TM * TN * 16;             // accumulator floats per lane
     static constexpr int RED = (KW - 1) * SPATIAL * 64 * ACC;  // split-k partials
-    static constexpr int A_TOTAL = BM * BK / 4, B_TOTAL = BK * BN / 4;  // 16-byte vectors
-    static constexpr int A_VECS = (A_TOTAL + THREADS - 1) / THREADS;     // per thread
-    static constexpr int B_VECS = (B_TOTAL + THREADS - 1) / THREADS;
     static constexpr int STEPS = BK / (8 * KW);          // 8-wide k steps per group per window
     static constexpr int MF = 4 * TM * TN;               // MFMAs per step
-    static constexpr int DSW = A_VECS + B_VECS;          // LDS writes per window
-    static constexpr int VMR = A_VECS + B_VECS;          // global loads per window
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tiling");
     static_assert(TM >= 1 && TM <= 4 && TN >= 1 && TN <= 4,
                   "a lane holds 1 to 4 adjacent rows or columns");
@@ -178,22 +190,40 @@ struct MfmaTile {
 template <class T, bool TA_, bool TB_, bool NARROW_ = true>
 struct Cfg : T {
     static constexpr bool TA = TA_, TB = TB_, NARROW = NARROW_;
+    // B as given whose lanes hold three adjacent columns (96-wide wave blocks) is
+    // copied in 12-byte pieces, one per lane's three columns, each into a 16-byte
+    // slot of its LDS row (the fourth float is zero and never read into an MFMA),
+    // so a fragment is one aligned 16-byte read instead of an 8-byte and a 4-byte
+    // one (2048 x 3072 x 4096: 142.1 -> 143.6 TFLOP/s, B transposed as the first
+    // operand: 139.3 -> 140.9).  The same form for A transposed with 96-high wave
+    // blocks measured 1.2-1.4% slower on the 192 x 128 block, so A keeps 16-byte
+    // copies.
+    static constexpr bool B3 = !TB && T::TN == 3;
+    static constexpr int AW = 4, BW = B3 ? 3 : 4;           // floats per copied vector
+    static constexpr int B_ROW = B3 ? T::BN / 3 * 4 : T::BN;  // LDS floats per B row
     static constexpr int PA = TA ? T::BM + T::PAD_B : T::BK + T::PAD_A;  // A window pitch
-    static constexpr int PB = TB ? T::BK + T::PAD_A : T::BN + T::PAD_B;  // B window pitch
+    static constexpr int PB = TB ? T::BK + T::PAD_A : B_ROW + T::PAD_B;  // B window pitch
     static constexpr int A_STAGE = (TA ? T::BK : T::BM) * PA;
     static constexpr int B_STAGE = (TB ? T::BN : T::BK) * PB;
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int LDS_FLOATS = T::STAGES * STAGE > T::RED ? T::STAGES * STAGE : T::RED;
+    // Copied vectors per window and per work-item.
+    static constexpr int A_TOTAL = T::BM * T::BK / AW, B_TOTAL = T::BK * T::BN / BW;
+    static constexpr int A_VECS = (A_TOTAL + T::THREADS - 1) / T::THREADS;
+    static constexpr int B_VECS = (B_TOTAL + T::THREADS - 1) / T::THREADS;
+    static constexpr int DSW = A_VECS + B_VECS;  // LDS writes per window
+    static constexpr int VMR = A_VECS + B_VECS;  // global loads per window
     static constexpr int DSR_A = TA ? 4 * lds_reads(T::TM) : T::TM;  // LDS reads per step
-    static constexpr int DSR_B = TB ? T::TN : 4 * lds_reads(T::TN);
+    static constexpr int DSR_B = TB ? T::TN : 4 * (B3 ? 1 : lds_reads(T::TN));
     static constexpr int DSR = DSR_A + DSR_B;
     // The steady-state loop writes LDS in the first step of a window and issues
     // the `vmr` global loads of a later window in the same step, or in the second
     // step when one step has too few MFMAs to cover all of those memory
     // instructions.
     static constexpr int load_step(int vmr) {
-        return (T::STEPS > 1 && T::MF < DSR + T::DSW + vmr) ? 1 : 0;
+        return (T::STEPS > 1 && T::MF < DSR + DSW + vmr) ? 1 : 0;
     }
+    static_assert(!B3 || T::BN % 3 == 0, "three-wide B rows");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 };
 
@@ -213,15 +243,17 @@ template <class T>
 using Acc = f32x16[T::TM][T::TN];
 
 // Global -> register -> LDS copy of one operand's k window, for the `VECS`
-// 16-byte vectors this work-item owns (vector v exists iff tid + v*THREADS <
-// TOTAL; a missing one re-reads the last vector and is not stored).
-//   k-contiguous (KC): ROWS rows (of op(A) or columns of op(B)) of BK floats;
-//     rows beyond `extent` read the last valid one.
-//   mn-contiguous: BK rows of COLS floats (along m or n); columns beyond
-//     `extent` read the last valid one.
-template <class T, bool KC, int ROWS_OR_COLS, int TOTAL, int VECS>
+// vectors of W floats this work-item owns (vector v exists iff tid + v*THREADS <
+// TOTAL; a missing one re-reads the last vector and is not stored).  Each vector
+// lands in a 16-byte slot of LDS (W = 3: the fourth float is zero).
+//   k-contiguous (KC, W = 4): ROWS rows (of op(A) or columns of op(B)) of BK
+//     floats; rows beyond `extent` read the last valid one.
+//   mn-contiguous (W = 4 or 3): BK rows of COLS floats (along m or n); columns
+//     beyond `extent` read the last valid one.
+template <class T, bool KC, int ROWS_OR_COLS, int TOTAL, int VECS, int W = 4>
 struct Operand {
-    static constexpr int Q = KC ? T::BK / 4 : ROWS_OR_COLS / 4;  // vectors per LDS row
+    static_assert(W == 4 || (W == 3 && !KC), "three-float vectors along m or n only");
+    static constexpr int Q = KC ? T::BK / 4 : ROWS_OR_COLS / W;  // vectors per LDS row
     const float *src[VECS];  // start of the vector in window 0 (when !NARROW)
     const char *org;         // uniform: the block's first row (KC) or column
     uint32_t off[VECS];      // byte offset of src[v] from org (when NARROW)
@@ -270,11 +302,11 @@ struct Operand {
                 kofs[v] = q * 4;
                 pos[v] = 0;
             } else {
-                src[v] = X + (int64_t)row * ld + origin + q * 4;
+                src[v] = X + (int64_t)row * ld + origin + q * W;
                 org = (const char *)(X + origin);
-                off[v] = (uint32_t)(((int64_t)row * ld + q * 4) * 4);
+                off[v] = (uint32_t)(((int64_t)row * ld + q * W) * 4);
                 kofs[v] = row;
-                pos[v] = origin + q * 4;
+                pos[v] = origin + q * W;
             }
             lds[v] = base + row * pitch + q * 4;
         }
@@ -289,8 +321,19 @@ struct Operand {
         }
     }
 
+    // W floats of row `row` (an mn row of the window) from column pos[v] on, each
+    // index clamped to extent - 1.
+    __device__ __forceinline__ f32x4 clamped(const float *row, int v, int extent) const {
+        f32x4 x;
+        x.x = row[min(pos[v] + 0, extent - 1)];
+        x.y = row[min(pos[v] + 1, extent - 1)];
+        x.z = row[min(pos[v] + 2, extent - 1)];
+        x.w = W == 4 ? row[min(pos[v] + 3, extent - 1)] : 0.0f;
+        return x;
+    }
+
     // Full window at k0 (every k < K).  INSIDE: every column of an mn-contiguous
-    // block lies inside its matrix, so whole 16-byte vectors are read.
+    // block lies inside its matrix, so whole vectors are read.
     template <bool INSIDE>
     __device__ __forceinline__ void fetch_full(int64_t k0, int64_t ld, int extent) {
 #pragma unroll
@@ -300,15 +343,12 @@ struct Operand {
             } else if constexpr (KC) {
                 r[v] = load16(src[v] + k0);
             } else if constexpr (INSIDE && T::NARROW) {
-                r[v] = load16_at(org + k0 * ld * 4, off[v]);
+                r[v] = W == 4 ? load16_at(org + k0 * ld * 4, off[v])
+                              : load12_at(org + k0 * ld * 4, off[v]);
             } else if constexpr (INSIDE) {
-                r[v] = load16(src[v] + k0 * ld);
+                r[v] = W == 4 ? load16(src[v] + k0 * ld) : load12(src[v] + k0 * ld);
             } else {
-                const float *row = at(v) + k0 * ld - pos[v];
-                r[v].x = row[min(pos[v] + 0, extent - 1)];
-                r[v].y = row[min(pos[v] + 1, extent - 1)];
-                r[v].z = row[min(pos[v] + 2, extent - 1)];
-                r[v].w = row[min(pos[v] + 3, extent - 1)];
+                r[v] = clamped(at(v) + k0 * ld - pos[v], v, extent);
             }
         }
     }
@@ -335,11 +375,7 @@ struct Operand {
                 r[v].w = kv > 3 ? p[3] : 0.0f;
             } else {
                 if (k0 + kofs[v] < K) {
-                    const float *row = at(v) + k0 * ld - pos[v];
-                    r[v].x = row[min(pos[v] + 0, extent - 1)];
-                    r[v].y = row[min(pos[v] + 1, extent - 1)];
-                    r[v].z = row[min(pos[v] + 2, extent - 1)];
-                    r[v].w = row[min(pos[v] + 3, extent - 1)];
+                    r[v] = clamped(at(v) + k0 * ld - pos[v], v, extent);
                 } else {
                     r[v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 }
@@ -361,8 +397,11 @@ struct Operand {
 template <class C>
 __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, int n0,
                                          int w_begin, int w_end, Acc<C> &acc) {
+    // mn-contiguous fragments: the lane's TM (TN) adjacent values of one k; with
+    // B3 the three values of B sit in a 16-byte slot.
     typedef typename VecOf<C::TM>::type AVec;
-    typedef typename VecOf<C::TN>::type BVec;
+    typedef typename std::conditional<C::B3, f32x4, typename VecOf<C::TN>::type>::type BVec;
+    constexpr int BL = C::B3 ? 4 : C::TN;  // lane_of width of B fragments
     const int M = g.M, N = g.N, K = g.K;
     const int64_t lda = g.lda, ldb = g.ldb;
     const int tid = threadIdx.x;
@@ -371,8 +410,8 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
     const int kg = wave / C::SPATIAL, sw = wave % C::SPATIAL;
     const int wm = sw / C::WAVES_N, wn = sw % C::WAVES_N;
 
-    Operand<C, !C::TA, C::BM, C::A_TOTAL, C::A_VECS> a;
-    Operand<C, C::TB, C::BN, C::B_TOTAL, C::B_VECS> b;
+    Operand<C, !C::TA, C::BM, C::A_TOTAL, C::A_VECS, C::AW> a;
+    Operand<C, C::TB, C::BN, C::B_TOTAL, C::B_VECS, C::BW> b;
     a.init(g.A, lda, m0, M, 0, C::PA, tid);
     b.init(g.B, ldb, n0, N, C::A_STAGE, C::PB, tid);
     // mn-contiguous blocks that reach past their matrix read clamped columns
@@ -394,7 +433,8 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
     const int a_frag = C::TA ? (4 * lh) * C::PA + wm * C::WM + C::TM * lr
                              : (wm * C::WM + lr) * C::PA + 4 * lh;
     const int b_frag = C::A_STAGE + (C::TB ? (wn * C::WN + lr) * C::PB + 4 * lh
-                                           : (4 * lh) * C::PB + wn * C::WN + C::TN * lr);
+                                           : (4 * lh) * C::PB + (C::B3 ? (wn * C::WN / 3 + lr) * 4
+                                                                       : wn * C::WN + C::TN * lr));
 
     // Fragments of one 8-wide k step.
     struct Frag {
@@ -436,7 +476,7 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
                     if constexpr (C::TB) {
                         bv = f.b[j][q];
                     } else {
-                        bv = lane_of<C::TN>(f.b[q], j);
+                        bv = lane_of<BL>(f.b[q], j);
                     }
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[i][j], 0, 0, 0);
                 }
@@ -469,7 +509,7 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
     // body free of branches there too.
     auto steady = [&](auto edge_tag) {
         constexpr bool EDGE = decltype(edge_tag)::value;
-        constexpr int VMR = EDGE ? (C::TA ? 4 : 1) * C::A_VECS + (C::TB ? 1 : 4) * C::B_VECS
+        constexpr int VMR = EDGE ? (C::TA ? 4 : 1) * C::A_VECS + (C::TB ? 1 : C::BW) * C::B_VECS
                                  : C::VMR;
         constexpr int LOAD_STEP = C::load_step(VMR);
         const int steady_end = min(w_end, K / C::BK) - C::STAGES;
