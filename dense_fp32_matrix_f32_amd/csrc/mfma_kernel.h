@@ -483,16 +483,36 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
     };
 
     // Prologue: the first STAGES-1 windows go to LDS, the next one to registers.
-    fetch((int64_t)w_begin * C::BK);
-    stash(0);
-    if constexpr (C::STAGES == 3) {
-        if (w_begin + 1 < w_end) {
-            fetch((int64_t)(w_begin + 1) * C::BK);
-            stash(1);
+    // Every load of these windows is issued before any of them is waited for (a
+    // second register set holds window w_begin + 1), so the first MFMA waits for
+    // one memory round trip, not one per window.
+    {
+        auto a1 = a;
+        auto b1 = b;
+        const bool second = w_begin + 1 < w_end;
+        fetch((int64_t)w_begin * C::BK);
+        if (second) {
+            a1.fetch((int64_t)(w_begin + 1) * C::BK, lda, M, K, a_inside);
+            b1.fetch((int64_t)(w_begin + 1) * C::BK, ldb, N, K, b_inside);
+        }
+        stash(0);
+        if constexpr (C::STAGES == 3) {
+            if (w_begin + 2 < w_end) fetch((int64_t)(w_begin + 2) * C::BK);
+            if (second) {
+                float *s1 = lds + C::STAGE;
+                a1.stash(s1, tid);
+                b1.stash(s1, tid);
+            }
+        } else {
+            if (second) {
+#pragma unroll
+                for (int v = 0; v < C::A_VECS; ++v) a.r[v] = a1.r[v];
+#pragma unroll
+                for (int v = 0; v < C::B_VECS; ++v) b.r[v] = b1.r[v];
+            }
         }
     }
     __syncthreads();
-    if (w_begin + C::STAGES - 1 < w_end) fetch((int64_t)(w_begin + C::STAGES - 1) * C::BK);
 
     Frag frag[2];
     int cur = 0;  // LDS stage of window w
