@@ -617,7 +617,7 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
 // 4*lh + r%4 and MFMA column lr of that block, placed as described in the header.
 template <class C>
 __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, const Acc<C> &acc,
-                                           int m_lo, int n_lo) {
+                                           int m_lo, int n_lo, int r_first = 0, int r_count = 16) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 31, lh = lane >> 5;
     const int sw = wave % C::SPATIAL;
@@ -651,11 +651,14 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
         }
         __builtin_memcpy(dst + col0, v, sizeof(v));
     };
+    // registers [r_first, r_first + r_count) of each block belong to this wave
+    auto mine = [&](int r) { return r >= r_first && r < r_first + r_count; };
     if (full) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                if (!mine(r)) continue;
                 float *dst = Cm + (int64_t)row_of(i, r) * ldc;
                 if constexpr (!C::TB) {
                     put_row(dst, i, r);
@@ -679,7 +682,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = row_of(i, r);
-                if (row >= m_lo && row < M) {
+                if (mine(r) && row >= m_lo && row < M) {
                     float *dst = Cm + (int64_t)row * ldc;
                     if (row_inside) {
                         if constexpr (!C::TB) put_row(dst, i, r);
@@ -696,44 +699,86 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
     }
 }
 
-// Split-k inside the work-group: groups 1..KW-1 hand their partial blocks to
-// group 0 through LDS, which adds them in group order.  Returns true for the
-// waves that hold the finished block.
+// Split-k inside the work-group: the KW groups of waves that share a block of C
+// each finish RPG = 16/KW of the 16 accumulator registers of every 32x32 block,
+// group g registers [g*RPG, (g+1)*RPG).  Every wave writes the registers that the
+// other groups finish to LDS (16-byte accesses, lane-contiguous), and each group
+// adds the KW partials of its own registers in group order 0, 1, ..., KW-1, the
+// order one group adding them all would use, so the sum is the same bit for
+// bit.  All waves then store their own registers, so the reduction and the
+// stores are spread over every wave of the group.  Returns the first register
+// this wave stores; it stores RPG of them.
 template <class C>
-__device__ __forceinline__ bool kw_reduce(float *lds, Acc<C> &acc) {
-    if constexpr (C::KW == 1) {
-        return true;
-    } else {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int kg = wave / C::SPATIAL, sw = wave % C::SPATIAL;
-        float *red = lds + sw * 64 * C::ACC + lane;
-        constexpr int GROUP_STRIDE = C::SPATIAL * 64 * C::ACC;
-        if (kg > 0) {
-            float *dst = red + (kg - 1) * GROUP_STRIDE;
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dst[((i * C::TN + j) * 16 + r) * 64] = acc[i][j][r];
-        }
-        __syncthreads();
-        if (kg > 0) return false;
-#pragma unroll
-        for (int gi = 1; gi < C::KW; ++gi) {
-            const float *src = red + (gi - 1) * GROUP_STRIDE;
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[i][j][r] += src[((i * C::TN + j) * 16 + r) * 64];
-        }
-        return true;
+struct KwReduce {
+    static constexpr int RPG = 16 / C::KW;                  // registers per group
+    static constexpr int SLICE = C::TM * C::TN * RPG * 64;  // floats one wave hands one group
+    static_assert(C::KW == 1 || RPG % 4 == 0, "whole 16-byte register runs per group");
+
+    // Offset of register run (i, j, q) (registers 4q..4q+3 of the group's RPG) of
+    // the slice that group h hands group g, for spatial wave sw and this lane.
+    __device__ __forceinline__ static int at(int h, int g, int sw, int lane, int i, int j, int q) {
+        const int slot = h * (C::KW - 1) + (g < h ? g : g - 1);
+        return (slot * C::SPATIAL + sw) * SLICE + (((i * C::TN + j) * (RPG / 4) + q) * 64 + lane) * 4;
     }
-}
+
+    template <int G>
+    __device__ __forceinline__ static void finish(const float *lds, Acc<C> &acc, int sw, int lane) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int q = 0; q < RPG / 4; ++q) {
+                    f32x4 part[C::KW];
+#pragma unroll
+                    for (int h = 0; h < C::KW; ++h) {
+                        if (h == G) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) part[h][e] = acc[i][j][G * RPG + 4 * q + e];
+                        } else {
+                            part[h] = *(const f32x4 *)(lds + at(h, G, sw, lane, i, j, q));
+                        }
+                    }
+                    f32x4 sum = part[0];
+#pragma unroll
+                    for (int h = 1; h < C::KW; ++h) sum += part[h];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][G * RPG + 4 * q + e] = sum[e];
+                }
+    }
+
+    __device__ __forceinline__ static int run(float *lds, Acc<C> &acc) {
+        if constexpr (C::KW == 1) {
+            return 0;
+        } else {
+            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+            const int kg = wave / C::SPATIAL, sw = wave % C::SPATIAL;
+#pragma unroll
+            for (int g = 0; g < C::KW; ++g) {
+                if (g == kg) continue;
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                        for (int q = 0; q < RPG / 4; ++q) {
+                            f32x4 v;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][g * RPG + 4 * q + e];
+                            *(f32x4 *)(lds + at(kg, g, sw, lane, i, j, q)) = v;
+                        }
+            }
+            __syncthreads();
+            switch (kg) {
+            case 0: finish<0>(lds, acc, sw, lane); break;
+            case 1: finish<1>(lds, acc, sw, lane); break;
+            case 2: if constexpr (C::KW > 2) finish<2>(lds, acc, sw, lane); break;
+            default: if constexpr (C::KW > 3) finish<3>(lds, acc, sw, lane); break;
+            }
+            return kg * RPG;
+        }
+    }
+};
 
 template <class C>
 __device__ __forceinline__ void zero_acc(Acc<C> &acc) {
@@ -770,8 +815,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_kernel(GemmArgs g, in
     Acc<C> acc;
     zero_acc<C>(acc);
     mma_tile<C>(g, lds, m0, n0, 0, (g.K + C::BK - 1) / C::BK, acc);
-    if (!kw_reduce<C>(lds, acc)) return;
-    store_tile<C>(g, m0, n0, acc, m_lo, n_lo);
+    const int r_first = KwReduce<C>::run(lds, acc);
+    store_tile<C>(g, m0, n0, acc, m_lo, n_lo, r_first, KwReduce<C>::RPG);
 }
 
 // True when every per-lane byte offset from a block's first row or column
@@ -808,13 +853,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_splitk_kernel(GemmArg
     Acc<C> acc;
     zero_acc<C>(acc);
     mma_tile<C>(g, lds, m0, n0, wb, we, acc);
-    if (!kw_reduce<C>(lds, acc)) return;
+    const int r_first = KwReduce<C>::run(lds, acc);
     GemmArgs o = g;
     o.C = ws + (int64_t)slice * g.M * g.N;
     o.ldc = g.N;
     o.alpha = 1.0f;
     o.beta = 0.0f;
-    store_tile<C>(o, m0, n0, acc, m_lo, n_lo);
+    store_tile<C>(o, m0, n0, acc, m_lo, n_lo, r_first, KwReduce<C>::RPG);
 }
 
 template <class T, bool TA, bool TB>
