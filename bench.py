@@ -128,24 +128,33 @@ def make_inputs(torch, M, N, K, seed, dist="normal", layout=(0, 0)):
 
 def time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warmup, layout=(0, 0),
                  workspace=None, sclk_log=None):
-    """Warm-up, then `steps` timed launches: wall clock between two full
-    synchronisations, and per-launch HIP events on the launch stream.  With a
+    """Warm-up, then `steps` timed launches back to back.  Returns the wall clock
+    between two full synchronisations (seconds) and the average kernel time (ms):
+    one HIP event pair on the launch stream around all timed launches, divided by
+    their number.  No event sits between two launches: an event pair per launch
+    opens a gap of about 10 us between kernels, half of which it would count as
+    kernel time, while back-to-back launches run with no gap.  dB may be a list of
+    device tensors, used in turn (B rotated over several buffers).  With a
     workspace tensor, the product goes through sgemm_f32_ex_ws.  With a list as
-    sclk_log, the shader clock read while the timed launches run is appended."""
+    sclk_log, the clock readings sampled while the timed launches run are appended."""
     stream = torch.cuda.current_stream()
     ta, tb = layout
     lda, ldb, ldc = (M if ta else K), (K if tb else N), N
+    bufs = dB if isinstance(dB, (list, tuple)) else [dB]
+    turn = [0]
 
     def call():
+        b = bufs[turn[0] % len(bufs)].data_ptr()
+        turn[0] += 1
         if workspace is not None:
-            st = sg.sgemm_f32_ex_ws(ta, tb, M, N, K, 1.0, dA.data_ptr(), lda, dB.data_ptr(), ldb,
+            st = sg.sgemm_f32_ex_ws(ta, tb, M, N, K, 1.0, dA.data_ptr(), lda, b, ldb,
                                     0.0, dC.data_ptr(), ldc, workspace.data_ptr(),
                                     4 * workspace.numel(), stream.cuda_stream)
         elif layout == (0, 0):
-            st = sg.sgemm_f32_algo(M, N, K, dA.data_ptr(), lda, dB.data_ptr(), ldb,
+            st = sg.sgemm_f32_algo(M, N, K, dA.data_ptr(), lda, b, ldb,
                                    dC.data_ptr(), ldc, stream.cuda_stream, algo)
         else:
-            st = sg.sgemm_f32_ex_algo(ta, tb, M, N, K, 1.0, dA.data_ptr(), lda, dB.data_ptr(),
+            st = sg.sgemm_f32_ex_algo(ta, tb, M, N, K, 1.0, dA.data_ptr(), lda, b,
                                       ldb, 0.0, dC.data_ptr(), ldc, stream.cuda_stream, algo)
         if st != 0:
             raise sg.SgemmError(st)
@@ -153,21 +162,19 @@ def time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warmup, layout=(0,
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    sampler = ClockSampler(torch) if sclk_log is not None else None
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
         call()
-        ends[i].record(stream)
-    # read while the queued launches run (host enqueueing is far shorter than them)
-    sclk = gpu_sclk(torch) if sclk_log is not None else None
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if sclk_log is not None:
-        sclk_log.append(sclk)
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, kernel_ms
+    if sampler is not None:
+        sclk_log.append(sampler.stop())
+    return wall, start.elapsed_time(end) / steps
 
 
 def cpu_baseline(A, B, M, N, K, budget_s: float):
@@ -228,11 +235,10 @@ def ladder(torch, sg, M, N, K, args):
             continue
         # one probe launch sizes the warm-up and the timed count
         _, probe = time_product(torch, sg, M, N, K, dA, dB, dC, algo, 1, 1)
-        est = max(probe[0], 1e-3)
+        est = max(probe, 1e-3)
         warm = max(args.warmup, min(2000, int(300 / est)))
         steps = max(args.steps, min(2000, int(200 / est)))
-        _, kms = time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warm)
-        avg = sum(kms) / len(kms)
+        _, avg = time_product(torch, sg, M, N, K, dA, dB, dC, algo, steps, warm)
         print(json.dumps({"shape": [M, N, K], "algo": name, "kernel_ms_avg": round(avg, 5),
                           "tflops": round(flops / (avg * 1e-3) / 1e12, 3),
                           "pct_fp32_peak": round(100 * flops / (avg * 1e-3) / 1e12 /
@@ -255,35 +261,69 @@ def _check(status, sg):
         raise sg.SgemmError(status)
 
 
+def _sclk_path(torch):
+    p = torch.cuda.get_device_properties(0)
+    return (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
+            f"{p.pci_device_id:02x}.0/pp_dpm_sclk")
+
+
 def gpu_sclk(torch):
-    """Current shader clock level of device 0 as the driver reports it, or None."""
+    """The shader clock that the driver marks as current for device 0 (MHz), or None.
+    On MI355X this is the power controller's running average, which lags the clock
+    the kernels run at by about a second; the clock during a kernel comes from the
+    counters (GRBM_GUI_ACTIVE over the kernel time)."""
     try:
-        p = torch.cuda.get_device_properties(0)
-        path = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
-                f"{p.pci_device_id:02x}.0/pp_dpm_sclk")
-        with open(path) as f:
+        with open(_sclk_path(torch)) as f:
             for line in f:
                 if line.rstrip().endswith("*"):
-                    return line.split(":", 1)[1].strip(" *\n")
+                    return int(line.split(":", 1)[1].strip(" *\n").lower().replace("mhz", ""))
     except Exception:  # noqa: BLE001 -- informational only
         return None
     return None
 
 
-def timed_launches(torch, stream, launch, warm_ms=300.0, timed_ms=200.0, min_steps=20):
-    """Per-launch HIP-event times (ms) after a time-based warm-up."""
+class ClockSampler:
+    """Reads gpu_sclk every 2 ms on a host thread until stop(); returns the samples'
+    count, maximum and last value."""
+
+    def __init__(self, torch):
+        import threading
+        self.torch, self.samples, self.done = torch, [], False
+        self.thread = threading.Thread(target=self._run, daemon=True)
+        self.thread.start()
+
+    def _run(self):
+        while not self.done:
+            v = gpu_sclk(self.torch)
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(0.002)
+
+    def stop(self):
+        self.done = True
+        self.thread.join()
+        s = self.samples
+        return {"samples": len(s), "max_mhz": max(s) if s else None,
+                "last_mhz": s[-1] if s else None}
+
+
+def timed_launches(torch, stream, launch, warm_ms=300.0, timed_ms=200.0, min_steps=20,
+                   regions=5):
+    """Average kernel time (ms) of back-to-back launches, one value per region: a
+    time-based warm-up, then `regions` runs of launches, each timed by one HIP event
+    pair on the stream around the whole run (no event between two launches)."""
     def run(n):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        for a, b in ev:
-            a.record(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
             launch()
-            b.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in ev]
-    est = max(min(run(3)), 1e-3)
+        return a.elapsed_time(b) / n
+    est = max(run(3), 1e-3)
     run(max(1, min(20000, int(warm_ms / est))))
-    return run(max(min_steps, min(20000, int(timed_ms / est))))
+    n = max(min_steps, min(20000, int(timed_ms / est / regions)))
+    return [run(n) for _ in range(regions)], n * regions
 
 
 def config_report(torch, sg, args):
@@ -306,7 +346,7 @@ def config_report(torch, sg, args):
             if st != 0:
                 raise sg.SgemmError(st)
 
-        kms = timed_launches(torch, stream, launch)
+        kms, launches = timed_launches(torch, stream, launch)
         med = statistics.median(kms)
         flops, nbytes = algorithmic_flops(M, N, K), algorithmic_bytes(M, N, K)
         cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -317,7 +357,8 @@ def config_report(torch, sg, args):
                    m_main, n_main, K, cus)) if algo == sg.ALGO_MFMA else None,
                "blocks_cover": [m_main, n_main],
                "kernel_ms_median": round(med, 5), "kernel_ms_mean": round(sum(kms) / len(kms), 5),
-               "kernel_ms_min": round(min(kms), 5), "launches": len(kms),
+               "kernel_ms_min": round(min(kms), 5), "launches": launches,
+               "timing": "median, mean and minimum of 5 back-to-back runs' average",
                "tflops": round(flops / (med * 1e-3) / 1e12, 3),
                "pct_fp32_peak": round(100 * flops / (med * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 2),
                "gbs": round(nbytes / (med * 1e-3) / 1e9, 1),
@@ -332,7 +373,7 @@ def config_report(torch, sg, args):
             def rotated():
                 launch(bufs[turn[0] % len(bufs)].data_ptr())
                 turn[0] += 1
-            rms = timed_launches(torch, stream, rotated)
+            rms, _ = timed_launches(torch, stream, rotated)
             rmed = statistics.median(rms)
             rec["rotated"] = {"b_buffers": len(bufs), "bytes": 4 * K * N * len(bufs),
                               "kernel_ms_median": round(rmed, 5),
@@ -342,7 +383,7 @@ def config_report(torch, sg, args):
                                                     PEAK_HBM_GBS, 2)}
             del bufs
         if algo == sg.ALGO_MFMA:
-            sms = timed_launches(torch, stream, lambda: _check(sg.sgemm_f32_algo(
+            sms, _ = timed_launches(torch, stream, lambda: _check(sg.sgemm_f32_algo(
                 M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, stream.cuda_stream,
                 sg.ALGO_BF16X6), sg))
             rec["bf16x6"] = split_record(flops, statistics.median(sms))
@@ -388,15 +429,18 @@ def tile_sweep(torch, sg, shapes, args):
             if st != 0:
                 raise sg.SgemmError(st, "sgemm_f32_ex_mfma_tile")
 
-        def timed(tile, n):
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(n)]
-            for a, b in ev:
+        def timed(tile, n, regions=1):
+            """Per-region average kernel time of n back-to-back launches (ms)."""
+            out = []
+            for _ in range(regions):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                launch(tile)
+                for _ in range(n):
+                    launch(tile)
                 b.record(stream)
-            torch.cuda.synchronize()
-            return [a.elapsed_time(b) for a, b in ev]
+                torch.cuda.synchronize()
+                out.append(a.elapsed_time(b) / n)
+            return out
 
         auto = sg.sgemm_f32_mfma_select(M, N, K, torch.cuda.get_device_properties(0)
                                         .multi_processor_count)
@@ -406,12 +450,13 @@ def tile_sweep(torch, sg, shapes, args):
         for tile in range(sg.sgemm_f32_mfma_tiles()):
             est = max(min(timed(tile, 2)), 1e-3)
             timed(tile, max(2, min(2000, int(50 / est))))
-            kms = timed(tile, max(args.steps, min(2000, int(150 / est))))
+            n = max(args.steps, min(2000, int(150 / est))) // 5 + 1
+            kms = timed(tile, n, regions=5)
             avg = sum(kms) / len(kms)
             print(json.dumps({"shape": [M, N, K], "layout": args.layout, "tile": tile,
                               "name": sg.sgemm_f32_mfma_tile_name(tile), "chosen": tile == auto,
                               "kernel_ms_avg": round(avg, 5), "kernel_ms_min": round(min(kms), 5),
-                              "tflops": round(flops / (avg * 1e-3) / 1e12, 2), "steps": len(kms)}),
+                              "tflops": round(flops / (avg * 1e-3) / 1e12, 2), "steps": 5 * n}),
                   flush=True)
         del dA, dB, dC
 
@@ -420,10 +465,15 @@ def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=60)
     p.add_argument("--shape", default="8192,8192,8192", help="M,N,K of the timed product")
     p.add_argument("--algo", default="auto")
     p.add_argument("--seed", type=int, default=6)
+    p.add_argument("--dist", default="normal", choices=["normal", "uniform_pm1", "smallint"],
+                   help="distribution of the A and B entries")
+    p.add_argument("--rotate", type=int, default=1,
+                   help="rotate B over this many distinct buffers (5 x 64 MiB for 1x4096x4096 "
+                        "exceeds the 256 MB Infinity Cache, so B comes from HBM)")
     p.add_argument("--no-also", action="store_true", help="skip the 2048x3072x4096 product")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="CPU time budget of the oracle baseline (0 = skip)")
@@ -482,10 +532,19 @@ def main(argv=None):
         ladder(torch, sg, M, N, K, args)
         return
     algo = sg.ALGOS[args.algo]
-    print(f"[bench] generating {M}x{K} and {K}x{N} N(0,1) inputs (seed {args.seed})",
+    dist_name = {"normal": "N(0,1)", "uniform_pm1": "U[-1,1)", "smallint": "integers in [-4,4]"}
+    print(f"[bench] generating {M}x{K} and {K}x{N} {dist_name[args.dist]} inputs (seed {args.seed})",
           file=sys.stderr, flush=True)
     layout = (int(args.layout[0] == "T"), int(args.layout[1] == "T"))
-    A, B, dA, dB, dC = make_inputs(torch, M, N, K, args.seed, layout=layout)
+    A, B, dA, dB, dC = make_inputs(torch, M, N, K, args.seed, dist=args.dist, layout=layout)
+    dBs = [dB]
+    if args.rotate > 1:
+        import synthgen
+        ta_, tb_ = layout
+        for r in range(1, args.rotate):
+            dBs.append(torch.from_numpy(synthgen.matrix(N if tb_ else K, K if tb_ else N,
+                                                        seed=args.seed + 100 + r, stream=1,
+                                                        dist=args.dist)).cuda())
     chosen = sg.sgemm_f32_select(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N)
     if layout != (0, 0):
         chosen = sg.ALGO_MFMA
@@ -500,13 +559,12 @@ def main(argv=None):
     torch.cuda.synchronize()
     sclk_before = gpu_sclk(torch)
     sclk_timed = []
-    wall, kms = time_product(torch, sg, M, N, K, dA, dB, dC, algo, args.steps, args.warmup,
-                             layout, workspace=ws, sclk_log=sclk_timed)
+    wall, kavg = time_product(torch, sg, M, N, K, dA, dBs, dC, algo, args.steps, args.warmup,
+                              layout, workspace=ws, sclk_log=sclk_timed)
     sclk_after = gpu_sclk(torch)
     flops = algorithmic_flops(M, N, K)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (wall / args.steps) / 1e12
-    kavg = sum(kms) / len(kms)
     achieved = flops / (kavg * 1e-3) / 1e12
     rec = {
         "metric": "SGEMM TFLOP/s (2MNK/t) + % FP32 peak at 2048\u00d74096\u00d73072 and 8192\u00b3",
@@ -522,9 +580,11 @@ def main(argv=None):
         "dtype": "f32",
         "data": "synthetic",
         "pct_fp32_peak": round(100 * value / PEAK_FP32_TFLOPS, 2),
-        "config": {"workload": f"C=A*B fp32 row-major M={M} N={N} K={K}, A,B iid N(0,1) "
-                               f"seed {args.seed}" +
+        "config": {"workload": f"C=A*B fp32 row-major M={M} N={N} K={K}, A,B iid "
+                               f"{dist_name[args.dist]} seed {args.seed}" +
                                ("" if layout == (0, 0) else f", operands {args.layout}") +
+                               (f", B rotated over {args.rotate} buffers" if args.rotate > 1
+                                else "") +
                                (f", split-k workspace {4 * ws.numel()} bytes" if ws is not None
                                 else ""),
                    "M": M, "N": N, "K": K, "algo": sg.sgemm_f32_algo_name(used),
@@ -533,11 +593,14 @@ def main(argv=None):
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
                      "traffic": read_traffic() if (M, N, K, layout) == (8192, 8192, 8192, (0, 0))
                      else None,
-                     "kernel_ms_avg": round(kavg, 4), "kernel_ms_min": round(min(kms), 4),
+                     "kernel_ms_avg": round(kavg, 4),
                      "algorithmic_flops": flops, "algorithmic_bytes": algorithmic_bytes(M, N, K),
                      "intensity_flop_per_byte": round(intensity(M, N, K), 2)},
-        "sclk": {"before": sclk_before, "during_timed": sclk_timed[0] if sclk_timed else None,
-                 "after": sclk_after},
+        "sclk_smu_average_mhz": {"before": sclk_before,
+                                 "timed": sclk_timed[0] if sclk_timed else None,
+                                 "after": sclk_after,
+                                 "note": "driver-reported running average (lags the kernel's "
+                                         "clock); the kernel's clock is measured from counters"},
     }
     if used in (sg.ALGO_SKINNY, sg.ALGO_SKINNY_N):
         # few rows or columns: the product streams one operand, so HBM bounds it
@@ -547,12 +610,12 @@ def main(argv=None):
     if layout == (0, 0) and algo == sg.ALGO_AUTO and M > 8 and N > 8:
         # the same product on the split-precision rung (fp32 accuracy on the bf16
         # matrix cores), reported beside the fp32 result, never as the value
-        _, sms = time_product(torch, sg, M, N, K, dA, dB, dC, sg.ALGO_BF16X6, args.steps,
-                              args.warmup)
-        rec["bf16x6"] = split_record(flops, sum(sms) / len(sms))
+        _, savg = time_product(torch, sg, M, N, K, dA, dB, dC, sg.ALGO_BF16X6, args.steps,
+                               args.warmup)
+        rec["bf16x6"] = split_record(flops, savg)
         rec["bf16x6"]["note"] = ("fp32 product on bf16 matrix cores, operands split into three "
                                  "bf16 parts (six part products), fp32 accumulation")
-    del dA, dB, dC
+    del dA, dB, dC, dBs
     if not args.no_also:
         m2, n2, k2 = 2048, 3072, 4096
         print(f"[bench] timing {m2}x{n2}x{k2}", file=sys.stderr, flush=True)
@@ -562,9 +625,8 @@ def main(argv=None):
         est_ms = algorithmic_flops(m2, n2, k2) / 120e12 * 1e3
         warm2 = max(args.warmup, int(300 / est_ms))
         steps2 = max(args.steps, int(200 / est_ms))
-        w2, k2ms = time_product(torch, sg, m2, n2, k2, eA, eB, eC, sg.ALGO_AUTO, steps2, warm2)
+        w2, k2avg = time_product(torch, sg, m2, n2, k2, eA, eB, eC, sg.ALGO_AUTO, steps2, warm2)
         f2 = algorithmic_flops(m2, n2, k2)
-        k2avg = sum(k2ms) / len(k2ms)
         rec["also"] = {"workload": f"C=A*B fp32 row-major M={m2} N={n2} K={k2}, N(0,1) seed 3",
                        "steps": steps2, "warmup": warm2,
                        "value": round(f2 / (w2 / steps2) / 1e12, 3), "unit": "TFLOP/s",
