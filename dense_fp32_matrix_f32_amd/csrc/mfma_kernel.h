@@ -157,12 +157,13 @@ __device__ __forceinline__ void interleave() {
 // KW wave groups splitting k, GROUP_M tile-rows per ordering group, STAGES LDS
 // buffers (2 or 3), OCC the number of waves per SIMD that the register
 // allocation must allow, PAD_A / PAD_B the LDS row padding of k-contiguous and
-// mn-contiguous windows.
+// mn-contiguous windows, RING the register sets that carry windows from global
+// memory to LDS (a window's loads are issued RING windows before it is stored).
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int KW_, int GROUP_M_, int STAGES_ = 2,
-          int OCC_ = 1, int PAD_A_ = 4, int PAD_B_ = 8>
+          int OCC_ = 1, int PAD_A_ = 4, int PAD_B_ = 8, int RING_ = 1>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, KW = KW_;
-    static constexpr int GROUP_M = GROUP_M_, STAGES = STAGES_, OCC = OCC_;
+    static constexpr int GROUP_M = GROUP_M_, STAGES = STAGES_, OCC = OCC_, RING = RING_;
     static constexpr int PAD_A = PAD_A_, PAD_B = PAD_B_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int SPATIAL = WAVES_M * WAVES_N;    // waves per k group
@@ -181,6 +182,7 @@ struct MfmaTile {
     static_assert(PAD_A_ % 4 == 0 && PAD_B_ % 4 == 0, "16-byte aligned LDS rows");
     static_assert(STAGES == 2 || (STAGES == 3 && STEPS % 2 == 0),
                   "a three-stage ring carries fragments across windows in an even step count");
+    static_assert(RING >= 1 && RING <= 4, "one to four register sets");
 };
 
 // A tile configuration with the storage order of each operand: TA (op(A) is the
@@ -482,131 +484,286 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
                 }
     };
 
-    // Prologue: the first STAGES-1 windows go to LDS, the next one to registers.
-    // Every load of these windows is issued before any of them is waited for (a
-    // second register set holds window w_begin + 1), so the first MFMA waits for
-    // one memory round trip, not one per window.
-    {
-        auto a1 = a;
-        auto b1 = b;
-        const bool second = w_begin + 1 < w_end;
-        fetch((int64_t)w_begin * C::BK);
-        if (second) {
-            a1.fetch((int64_t)(w_begin + 1) * C::BK, lda, M, K, a_inside);
-            b1.fetch((int64_t)(w_begin + 1) * C::BK, ldb, N, K, b_inside);
-        }
-        stash(0);
-        if constexpr (C::STAGES == 3) {
-            if (w_begin + 2 < w_end) fetch((int64_t)(w_begin + 2) * C::BK);
+    if constexpr (C::RING == 1) {
+        // Prologue: the first STAGES-1 windows go to LDS, the next one to registers.
+        // Every load of these windows is issued before any of them is waited for (a
+        // second register set holds window w_begin + 1), so the first MFMA waits for
+        // one memory round trip, not one per window.
+        {
+            auto a1 = a;
+            auto b1 = b;
+            const bool second = w_begin + 1 < w_end;
+            fetch((int64_t)w_begin * C::BK);
             if (second) {
-                float *s1 = lds + C::STAGE;
-                a1.stash(s1, tid);
-                b1.stash(s1, tid);
+                a1.fetch((int64_t)(w_begin + 1) * C::BK, lda, M, K, a_inside);
+                b1.fetch((int64_t)(w_begin + 1) * C::BK, ldb, N, K, b_inside);
             }
+            stash(0);
+            if constexpr (C::STAGES == 3) {
+                if (w_begin + 2 < w_end) fetch((int64_t)(w_begin + 2) * C::BK);
+                if (second) {
+                    float *s1 = lds + C::STAGE;
+                    a1.stash(s1, tid);
+                    b1.stash(s1, tid);
+                }
+            } else {
+                if (second) {
+    #pragma unroll
+                    for (int v = 0; v < C::A_VECS; ++v) a.r[v] = a1.r[v];
+    #pragma unroll
+                    for (int v = 0; v < C::B_VECS; ++v) b.r[v] = b1.r[v];
+                }
+            }
+        }
+        __syncthreads();
+
+        Frag frag[2];
+        int cur = 0;  // LDS stage of window w
+        int w = w_begin;
+        if constexpr (C::STAGES == 3) read_frag(frag[0], lds, 0);
+
+        // Steady state: a window whose successors up to w + STAGES are all full.
+        // The body has no branches, so the copies of later windows (LDS stores of
+        // window w + STAGES - 1, global loads of window w + STAGES) and the fragment
+        // reads of the next step are spread one by one between the MFMAs instead of
+        // stalling the matrix cores in a block of their own.  Work-groups whose
+        // block reaches past M or N on an mn-contiguous operand (EDGE) load that
+        // operand one element at a time with the index clamped, which keeps the
+        // body free of branches there too.
+        auto steady = [&](auto edge_tag) {
+            constexpr bool EDGE = decltype(edge_tag)::value;
+            constexpr int VMR = EDGE ? (C::TA ? 4 : 1) * C::A_VECS + (C::TB ? 1 : C::BW) * C::B_VECS
+                                     : C::VMR;
+            constexpr int LOAD_STEP = C::load_step(VMR);
+            const int steady_end = min(w_end, K / C::BK) - C::STAGES;
+            for (; w < steady_end; ++w) {
+                const float *s = lds + cur * C::STAGE;
+                const int next = cur + 1 == C::STAGES ? 0 : cur + 1;
+                const int fill = cur == 0 ? C::STAGES - 1 : cur - 1;
+                if constexpr (C::STAGES == 2) read_frag(frag[0], s, 0);
+    #pragma unroll
+                for (int t = 0; t < C::STEPS; ++t) {
+                    if (t + 1 < C::STEPS) {
+                        read_frag(frag[(t + 1) & 1], s, t + 1);
+                    } else if constexpr (C::STAGES == 3) {
+                        read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
+                    }
+                    if (t == 0) stash(fill);
+                    if (t == LOAD_STEP) {
+                        const int64_t k0 = (int64_t)(w + C::STAGES) * C::BK;
+                        a.template fetch_full<!EDGE>(k0, lda, M);
+                        b.template fetch_full<!EDGE>(k0, ldb, N);
+                    }
+                    multiply(frag[t & 1]);
+                    // LDS reads issued in step 0, in a middle step and in the last step.
+                    constexpr int R0 = (1 < C::STEPS || C::STAGES == 3) ? C::DSR : 0;
+                    constexpr int RL = C::STAGES == 3 ? C::DSR : 0;
+                    constexpr int R1 = 2 < C::STEPS ? C::DSR : RL;
+                    constexpr int VM0 = LOAD_STEP == 0 ? VMR : 0;
+                    if (t == 0) {
+                        interleave<C::MF, R0, C::DSW, VM0>();
+                    } else if (t == LOAD_STEP) {
+                        interleave<C::MF, R1, 0, VMR>();
+                    } else if (t + 1 < C::STEPS) {
+                        interleave<C::MF, C::DSR, 0, 0>();
+                    } else {
+                        interleave<C::MF, RL, 0, 0>();
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                __syncthreads();
+                cur = next;
+            }
+        };
+        if (interior) {
+            steady(std::false_type{});
         } else {
-            if (second) {
-#pragma unroll
-                for (int v = 0; v < C::A_VECS; ++v) a.r[v] = a1.r[v];
-#pragma unroll
-                for (int v = 0; v < C::B_VECS; ++v) b.r[v] = b1.r[v];
-            }
+            steady(std::true_type{});
         }
-    }
-    __syncthreads();
 
-    Frag frag[2];
-    int cur = 0;  // LDS stage of window w
-    int w = w_begin;
-    if constexpr (C::STAGES == 3) read_frag(frag[0], lds, 0);
-
-    // Steady state: a window whose successors up to w + STAGES are all full.
-    // The body has no branches, so the copies of later windows (LDS stores of
-    // window w + STAGES - 1, global loads of window w + STAGES) and the fragment
-    // reads of the next step are spread one by one between the MFMAs instead of
-    // stalling the matrix cores in a block of their own.  Work-groups whose
-    // block reaches past M or N on an mn-contiguous operand (EDGE) load that
-    // operand one element at a time with the index clamped, which keeps the
-    // body free of branches there too.
-    auto steady = [&](auto edge_tag) {
-        constexpr bool EDGE = decltype(edge_tag)::value;
-        constexpr int VMR = EDGE ? (C::TA ? 4 : 1) * C::A_VECS + (C::TB ? 1 : C::BW) * C::B_VECS
-                                 : C::VMR;
-        constexpr int LOAD_STEP = C::load_step(VMR);
-        const int steady_end = min(w_end, K / C::BK) - C::STAGES;
-        for (; w < steady_end; ++w) {
+        // Remaining windows (the last STAGES ones and a partial last window): the
+        // same schedule with the copies guarded.
+        for (; w < w_end; ++w) {
             const float *s = lds + cur * C::STAGE;
             const int next = cur + 1 == C::STAGES ? 0 : cur + 1;
-            const int fill = cur == 0 ? C::STAGES - 1 : cur - 1;
             if constexpr (C::STAGES == 2) read_frag(frag[0], s, 0);
-#pragma unroll
+    #pragma unroll
             for (int t = 0; t < C::STEPS; ++t) {
+                // Issue the reads of the following step before this step's MFMAs.  After
+                // the last window the cross-window read fetches an unused stage; keeping
+                // it unconditional lets the LDS wait counts stay exact.
                 if (t + 1 < C::STEPS) {
                     read_frag(frag[(t + 1) & 1], s, t + 1);
                 } else if constexpr (C::STAGES == 3) {
                     read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
                 }
-                if (t == 0) stash(fill);
-                if (t == LOAD_STEP) {
-                    const int64_t k0 = (int64_t)(w + C::STAGES) * C::BK;
-                    a.template fetch_full<!EDGE>(k0, lda, M);
-                    b.template fetch_full<!EDGE>(k0, ldb, N);
-                }
-                multiply(frag[t & 1]);
-                // LDS reads issued in step 0, in a middle step and in the last step.
-                constexpr int R0 = (1 < C::STEPS || C::STAGES == 3) ? C::DSR : 0;
-                constexpr int RL = C::STAGES == 3 ? C::DSR : 0;
-                constexpr int R1 = 2 < C::STEPS ? C::DSR : RL;
-                constexpr int VM0 = LOAD_STEP == 0 ? VMR : 0;
-                if (t == 0) {
-                    interleave<C::MF, R0, C::DSW, VM0>();
-                } else if (t == LOAD_STEP) {
-                    interleave<C::MF, R1, 0, VMR>();
-                } else if (t + 1 < C::STEPS) {
-                    interleave<C::MF, C::DSR, 0, 0>();
-                } else {
-                    interleave<C::MF, RL, 0, 0>();
-                }
                 __builtin_amdgcn_sched_barrier(0);
+                multiply(frag[t & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // Window w + STAGES - 1 goes from registers to the stage freed by window w - 1,
+            // and the loads of the window after it are issued.
+            if (w + C::STAGES - 1 < w_end) {
+                const int fill = cur == 0 ? C::STAGES - 1 : cur - 1;
+                stash(fill);
+                if (w + C::STAGES < w_end) fetch((int64_t)(w + C::STAGES) * C::BK);
             }
             __syncthreads();
             cur = next;
         }
-    };
-    if (interior) {
-        steady(std::false_type{});
     } else {
-        steady(std::true_type{});
-    }
-
-    // Remaining windows (the last STAGES ones and a partial last window): the
-    // same schedule with the copies guarded.
-    for (; w < w_end; ++w) {
-        const float *s = lds + cur * C::STAGE;
-        const int next = cur + 1 == C::STAGES ? 0 : cur + 1;
-        if constexpr (C::STAGES == 2) read_frag(frag[0], s, 0);
+        // Register ring.  Window i (counted from w_begin) is carried from its loads
+        // to its LDS store by register set i % RING.  In the window that stores
+        // window i + STAGES - 1 (from set Q) the loads of window i + STAGES - 1 +
+        // RING go into the same set, so every window's loads have RING windows to
+        // arrive instead of one.  The loop runs in groups of RING windows so that
+        // each set index is a constant.
+        constexpr int S = C::STAGES, R = C::RING;
+        const int n = w_end - w_begin;
+        decltype(a) as[R];
+        decltype(b) bs[R];
 #pragma unroll
-        for (int t = 0; t < C::STEPS; ++t) {
-            // Issue the reads of the following step before this step's MFMAs.  After
-            // the last window the cross-window read fetches an unused stage; keeping
-            // it unconditional lets the LDS wait counts stay exact.
-            if (t + 1 < C::STEPS) {
-                read_frag(frag[(t + 1) & 1], s, t + 1);
-            } else if constexpr (C::STAGES == 3) {
-                read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            multiply(frag[t & 1]);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < R; ++q) {
+            as[q] = a;
+            bs[q] = b;
         }
-        // Window w + STAGES - 1 goes from registers to the stage freed by window w - 1,
-        // and the loads of the window after it are issued.
-        if (w + C::STAGES - 1 < w_end) {
-            const int fill = cur == 0 ? C::STAGES - 1 : cur - 1;
-            stash(fill);
-            if (w + C::STAGES < w_end) fetch((int64_t)(w + C::STAGES) * C::BK);
+        auto win_k0 = [&](int i) { return (int64_t)(w_begin + i) * C::BK; };
+        // Prologue: windows 0 .. S-2 into LDS stages 0 .. S-2 through temporaries,
+        // windows S-1 .. S-2+R into their ring sets; every load issued before any
+        // is waited for.
+        {
+            decltype(a) pa[S - 1];
+            decltype(b) pb[S - 1];
+#pragma unroll
+            for (int j = 0; j < S - 1; ++j) {
+                pa[j] = a;
+                pb[j] = b;
+                if (j < n) {
+                    pa[j].fetch(win_k0(j), lda, M, K, a_inside);
+                    pb[j].fetch(win_k0(j), ldb, N, K, b_inside);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                if (S - 1 + u < n) {
+                    as[(S - 1 + u) % R].fetch(win_k0(S - 1 + u), lda, M, K, a_inside);
+                    bs[(S - 1 + u) % R].fetch(win_k0(S - 1 + u), ldb, N, K, b_inside);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < S - 1; ++j) {
+                if (j < n) {
+                    float *st = lds + j * C::STAGE;
+                    pa[j].stash(st, tid);
+                    pb[j].stash(st, tid);
+                }
+            }
         }
         __syncthreads();
-        cur = next;
+
+        Frag frag[2];
+        int cur = 0;  // LDS stage of the current window
+        if constexpr (S == 3) read_frag(frag[0], lds, 0);
+        // Windows whose ring loads (window i + S - 1 + R) are full windows run the
+        // branch-free schedule; the rest guard their stores and loads.
+        const int steady_n = min(n, K / C::BK - w_begin) - S - R + 1;
+
+        auto window = [&](auto q_tag, auto edge_tag, auto steady_tag, int i) {
+            constexpr int Q = decltype(q_tag)::value;
+            constexpr bool EDGE = decltype(edge_tag)::value;
+            constexpr bool STEADY = decltype(steady_tag)::value;
+            constexpr int VMR = EDGE ? (C::TA ? 4 : 1) * C::A_VECS + (C::TB ? 1 : C::BW) * C::B_VECS
+                                     : C::VMR;
+            constexpr int LOAD_STEP = C::load_step(VMR);
+            const float *sp = lds + cur * C::STAGE;
+            const int next = cur + 1 == S ? 0 : cur + 1;
+            const int fill = cur == 0 ? S - 1 : cur - 1;
+            float *fill_stage = lds + fill * C::STAGE;
+            if constexpr (S == 2) read_frag(frag[0], sp, 0);
+#pragma unroll
+            for (int t = 0; t < C::STEPS; ++t) {
+                if (t + 1 < C::STEPS) {
+                    read_frag(frag[(t + 1) & 1], sp, t + 1);
+                } else if constexpr (S == 3) {
+                    read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
+                }
+                if constexpr (STEADY) {
+                    if (t == 0) {
+                        as[Q].stash(fill_stage, tid);
+                        bs[Q].stash(fill_stage, tid);
+                    }
+                    if (t == LOAD_STEP) {
+                        const int64_t k0 = win_k0(i + S - 1 + R);
+                        as[Q].template fetch_full<!EDGE>(k0, lda, M);
+                        bs[Q].template fetch_full<!EDGE>(k0, ldb, N);
+                    }
+                    multiply(frag[t & 1]);
+                    constexpr int R0 = (1 < C::STEPS || S == 3) ? C::DSR : 0;
+                    constexpr int RL = S == 3 ? C::DSR : 0;
+                    constexpr int R1 = 2 < C::STEPS ? C::DSR : RL;
+                    constexpr int VM0 = LOAD_STEP == 0 ? VMR : 0;
+                    if (t == 0) {
+                        interleave<C::MF, R0, C::DSW, VM0>();
+                    } else if (t == LOAD_STEP) {
+                        interleave<C::MF, R1, 0, VMR>();
+                    } else if (t + 1 < C::STEPS) {
+                        interleave<C::MF, C::DSR, 0, 0>();
+                    } else {
+                        interleave<C::MF, RL, 0, 0>();
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                } else {
+                    __builtin_amdgcn_sched_barrier(0);
+                    multiply(frag[t & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if constexpr (!STEADY) {
+                if (i + S - 1 < n) {
+                    as[Q].stash(fill_stage, tid);
+                    bs[Q].stash(fill_stage, tid);
+                    if (i + S - 1 + R < n) {
+                        as[Q].fetch(win_k0(i + S - 1 + R), lda, M, K, a_inside);
+                        bs[Q].fetch(win_k0(i + S - 1 + R), ldb, N, K, b_inside);
+                    }
+                }
+            }
+            __syncthreads();
+            cur = next;
+        };
+        // Whole groups of R steady windows run in a loop with no branch between a
+        // set's loads and its store, issuing the sets' loads in the prologue's order,
+        // so each store waits only for its own set; the windows after them (fewer
+        // than R that could still be steady, and the last S - 1 + R) take the
+        // guarded form.
+        auto run = [&](auto edge_tag) {
+            int i0 = 0;
+            auto group = [&](auto steady_tag) {
+                auto one = [&](auto u_tag) {
+                    constexpr int U = decltype(u_tag)::value;
+                    if constexpr (U < R) {
+                        using Qt = std::integral_constant<int, (U + S - 1) % R>;
+                        if constexpr (decltype(steady_tag)::value) {
+                            window(Qt{}, edge_tag, steady_tag, i0 + U);
+                        } else if (i0 + U < n) {
+                            window(Qt{}, edge_tag, steady_tag, i0 + U);
+                        }
+                    }
+                };
+                one(std::integral_constant<int, 0>{});
+                one(std::integral_constant<int, 1>{});
+                one(std::integral_constant<int, 2>{});
+                one(std::integral_constant<int, 3>{});
+            };
+            const int steady_groups = steady_n > 0 ? steady_n / R : 0;
+            for (int g = 0; g < steady_groups; ++g, i0 += R) group(std::true_type{});
+            for (; i0 < n; i0 += R) group(std::false_type{});
+        };
+        if (interior) {
+            run(std::false_type{});
+        } else {
+            run(std::true_type{});
+        }
     }
 }
 
@@ -906,9 +1063,12 @@ using TileSplit192 = MfmaTile<128, 192, 32, 64, 96, 2, 8, 3>;
 // 192 x 128 blocks of 96 x 64 per wave.
 using TileTall = MfmaTile<192, 128, 16, 96, 64, 1, 8, 3>;
 using TileSmall = MfmaTile<64, 64, 16, 32, 32, 1, 4, 3>;
-using TileSplit64 = MfmaTile<64, 64, 32, 32, 32, 2, 4, 3>;
-// k split four ways: one 8-wide step per group and window, so two stages.
-using TileTiny = MfmaTile<32, 32, 32, 32, 32, 4, 4, 2>;
+// Three register sets carry its windows from global memory to LDS, so each
+// window's loads have three windows to arrive (1024^3: 23.9 -> 22.3 us).
+using TileSplit64 = MfmaTile<64, 64, 32, 32, 32, 2, 4, 3, 1, 4, 8, 3>;
+// k split four ways: one 8-wide step per group and window, so two stages; two
+// register sets (512^3: 8.9 -> 8.7 us).
+using TileTiny = MfmaTile<32, 32, 32, 32, 32, 4, 4, 2, 1, 4, 8, 2>;
 // The same block with 64-wide windows and three stages: twice the work per
 // window and one more window in flight, for grids of at most one block per CU
 // over a long k, where TileTiny waits on its loads (512 x 512 x 32768: 352 ->
