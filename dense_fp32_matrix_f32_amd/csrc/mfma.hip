@@ -1,6 +1,7 @@
 // mfma.hip -- the matrix-core rung: tile table, cost-model choice and dispatch
 // to the kernels of mfma_kernel.h (instantiated per operand storage order in
 // mfma_nn.hip, mfma_nt.hip, mfma_tn.hip and mfma_tt.hip).
+#include <atomic>
 #include <cmath>
 
 #include "mfma_kernel.h"
@@ -53,12 +54,17 @@ static_assert(kTiles[5].bm == TileSplit64::BM && kTiles[5].bn == TileSplit64::BN
 static_assert(kTiles[6].bm == TileTiny::BM && kTiles[6].bn == TileTiny::BN, "row 6");
 static_assert(kTiles[7].bm == TileTiny64::BM && kTiles[7].bn == TileTiny64::BN, "row 7");
 
+// Compute units of the current device, looked up once per device (256 if the
+// query fails, as on a host without a GPU).
 int compute_units() {
+    static std::atomic<int> known[64];
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64 && (cus = known[dev].load(std::memory_order_relaxed)) > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
-        cus = 256;
+        return 256;
+    if (dev >= 0 && dev < 64) known[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 

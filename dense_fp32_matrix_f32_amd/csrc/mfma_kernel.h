@@ -188,10 +188,12 @@ struct MfmaTile {
 // A tile configuration with the storage order of each operand: TA (op(A) is the
 // transpose of the stored K x M array) and TB (op(B) is the transpose of the
 // stored N x K array); NARROW: every per-lane byte offset inside a block window
-// fits 32 bits (checked on the host by narrow_offsets()).
-template <class T, bool TA_, bool TB_, bool NARROW_ = true>
+// fits 32 bits (checked on the host by narrow_offsets()); RING: the register sets
+// of this instantiation (the tile's RING, or 1, chosen per launch by use_ring()).
+template <class T, bool TA_, bool TB_, bool NARROW_ = true, int RING_ = T::RING>
 struct Cfg : T {
     static constexpr bool TA = TA_, TB = TB_, NARROW = NARROW_;
+    static constexpr int RING = RING_;  // register sets used by this instantiation
     // B as given whose lanes hold three adjacent columns (96-wide wave blocks) is
     // copied in 12-byte pieces, one per lane's three columns, each into a 16-byte
     // slot of its LDS row (the fourth float is zero and never read into an MFMA),
@@ -757,7 +759,43 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
             };
             const int steady_groups = steady_n > 0 ? steady_n / R : 0;
             for (int g = 0; g < steady_groups; ++g, i0 += R) group(std::true_type{});
-            for (; i0 < n; i0 += R) group(std::false_type{});
+            // steady windows that do not fill a whole group
+            const int rest = steady_n > 0 ? steady_n - steady_groups * R : 0;
+            auto rest_one = [&](auto u_tag) {
+                constexpr int U = decltype(u_tag)::value;
+                if constexpr (U + 1 < R) {
+                    if (U < rest) {
+                        using Qt = std::integral_constant<int, (U + S - 1) % R>;
+                        window(Qt{}, edge_tag, std::true_type{}, i0 + U);
+                    }
+                }
+            };
+            rest_one(std::integral_constant<int, 0>{});
+            rest_one(std::integral_constant<int, 1>{});
+            rest_one(std::integral_constant<int, 2>{});
+            // the guarded windows continue the set cycle where the steady ones stopped
+            auto tail_from = [&](auto r_tag) {
+                constexpr int R0 = decltype(r_tag)::value;
+                for (int i = i0 + R0; i < n; i += R) {
+                    auto one = [&](auto u_tag) {
+                        constexpr int U = decltype(u_tag)::value;
+                        if constexpr (U < R) {
+                            using Qt = std::integral_constant<int, (R0 + U + S - 1) % R>;
+                            if (i + U < n) window(Qt{}, edge_tag, std::false_type{}, i + U);
+                        }
+                    };
+                    one(std::integral_constant<int, 0>{});
+                    one(std::integral_constant<int, 1>{});
+                    one(std::integral_constant<int, 2>{});
+                    one(std::integral_constant<int, 3>{});
+                }
+            };
+            switch (rest) {
+            case 0: tail_from(std::integral_constant<int, 0>{}); break;
+            case 1: if constexpr (R > 1) tail_from(std::integral_constant<int, 1>{}); break;
+            case 2: if constexpr (R > 2) tail_from(std::integral_constant<int, 2>{}); break;
+            default: if constexpr (R > 3) tail_from(std::integral_constant<int, 3>{}); break;
+            }
         };
         if (interior) {
             run(std::false_type{});
@@ -1019,62 +1057,92 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void mfma_splitk_kernel(GemmArg
     store_tile<C>(o, m0, n0, acc, m_lo, n_lo, r_first, KwReduce<C>::RPG);
 }
 
+// Whether a launch of `blocks` work-groups, each over `windows` k windows, uses
+// the tile's register ring.  The ring lets a block's loads run several windows
+// ahead, which pays when the wait for each window's loads sets the pace: one
+// round of blocks over a long k (1024^3 on 64 x 64 blocks -9%, 512 x 512 x 32768
+// on 32 x 32 x 64 blocks -25%), or several rounds over a very long one (256 x
+// 8192 x 8192, 256 windows in two rounds, -7%; 1000 x 5000 x 2000, 125 windows
+// in five rounds, -5%).  It costs a longer prologue and more guarded windows at
+// the end, which lose on short k (4096 x 4096 x 256 on 128 x 128 blocks, 16
+// windows, +14%) and on grids of several rounds over a moderate k (6000 x 6000
+// x 1000, 63 windows, +3%; 4095 x 4097 x 1023 on 192 x 128 blocks +1.4%).
+template <class T>
+bool use_ring(int64_t blocks, int64_t windows) {
+    return T::RING > 1 && windows >= 16 && (blocks <= compute_units() || windows >= 96);
+}
+
+template <class T, bool TA, bool TB, int R>
+hipError_t launch_tile_r(const Problem &p, hipStream_t s, int64_t tiles_m, int64_t tiles_n) {
+    const GemmArgs g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(T::THREADS);
+    if (narrow_offsets<T, TA, TB>(p))
+        return launch(mfma_kernel<Cfg<T, TA, TB, true, R>>, grid, block, 0, s, g, (int)tiles_m,
+                      (int)tiles_n);
+    return launch(mfma_kernel<Cfg<T, TA, TB, false, R>>, grid, block, 0, s, g, (int)tiles_m,
+                  (int)tiles_n);
+}
+
 template <class T, bool TA, bool TB>
 hipError_t launch_tile(const Problem &p, hipStream_t s) {
-    using C = Cfg<T, TA, TB>;
-    const int64_t tiles_m = (p.M + C::BM - 1) / C::BM;
-    const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
+    const int64_t tiles_m = (p.M + T::BM - 1) / T::BM;
+    const int64_t tiles_n = (p.N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n > INT32_MAX) return hipErrorInvalidValue;
-    const GemmArgs g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(C::THREADS);
-    if (narrow_offsets<T, TA, TB>(p))
-        return launch(mfma_kernel<Cfg<T, TA, TB, true>>, grid, block, 0, s, g, (int)tiles_m,
-                      (int)tiles_n);
-    return launch(mfma_kernel<Cfg<T, TA, TB, false>>, grid, block, 0, s, g, (int)tiles_m,
-                  (int)tiles_n);
+    if constexpr (T::RING > 1) {
+        if (use_ring<T>(tiles_m * tiles_n, ((int64_t)p.K + T::BK - 1) / T::BK))
+            return launch_tile_r<T, TA, TB, T::RING>(p, s, tiles_m, tiles_n);
+    }
+    return launch_tile_r<T, TA, TB, 1>(p, s, tiles_m, tiles_n);
 }
 
 // The split-k form of configuration T with `slices` slices; the caller has checked
 // that every slice holds at least one k window and that the workspace holds
 // slices * M * N floats.
+template <class T, bool TA, bool TB, int R>
+hipError_t launch_tile_splitk_r(const Problem &p, hipStream_t s, int slices, float *ws,
+                                int64_t tiles_m, int64_t tiles_n) {
+    const GemmArgs g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
+    const dim3 grid((unsigned)(tiles_m * tiles_n * slices)), block(T::THREADS);
+    if (narrow_offsets<T, TA, TB>(p))
+        return launch(mfma_splitk_kernel<Cfg<T, TA, TB, true, R>>, grid, block, 0, s, g,
+                      (int)tiles_m, (int)tiles_n, slices, ws);
+    return launch(mfma_splitk_kernel<Cfg<T, TA, TB, false, R>>, grid, block, 0, s, g,
+                  (int)tiles_m, (int)tiles_n, slices, ws);
+}
+
 template <class T, bool TA, bool TB>
 hipError_t launch_tile_splitk(const Problem &p, hipStream_t s, int slices, float *ws) {
-    using C = Cfg<T, TA, TB>;
-    const int64_t tiles_m = (p.M + C::BM - 1) / C::BM;
-    const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
+    const int64_t tiles_m = (p.M + T::BM - 1) / T::BM;
+    const int64_t tiles_n = (p.N + T::BN - 1) / T::BN;
     if (tiles_m * tiles_n * slices > INT32_MAX) return hipErrorInvalidValue;
-    const GemmArgs g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.alpha, p.beta};
-    const dim3 grid((unsigned)(tiles_m * tiles_n * slices)), block(C::THREADS);
-    if (narrow_offsets<T, TA, TB>(p))
-        return launch(mfma_splitk_kernel<Cfg<T, TA, TB, true>>, grid, block, 0, s, g, (int)tiles_m,
-                      (int)tiles_n, slices, ws);
-    return launch(mfma_splitk_kernel<Cfg<T, TA, TB, false>>, grid, block, 0, s, g, (int)tiles_m,
-                  (int)tiles_n, slices, ws);
+    if constexpr (T::RING > 1) {
+        const int64_t windows = ((int64_t)p.K + T::BK - 1) / T::BK / slices;
+        if (use_ring<T>(tiles_m * tiles_n * slices, windows))
+            return launch_tile_splitk_r<T, TA, TB, T::RING>(p, s, slices, ws, tiles_m, tiles_n);
+    }
+    return launch_tile_splitk_r<T, TA, TB, 1>(p, s, slices, ws, tiles_m, tiles_n);
 }
 
 // ---------------------------------------------------------------------------
 // Tile configurations.
 // 256 x 256 blocks, one wave per SIMD with 128 x 128 of C each: large products.
 using TileHuge = MfmaTile<256, 256, 16, 128, 128, 1, 8, 3>;
-using TileWide = MfmaTile<128, 128, 16, 32, 128, 1, 8, 3>;
+using TileWide = MfmaTile<128, 128, 16, 32, 128, 1, 8, 3, 1, 4, 8, 3>;
 // 128 x 192 blocks of 64 x 96 per wave, k split over two wave groups (two waves
 // per SIMD): one block per CU on grids of about 256 blocks, such as 2048 x 3072.
 using TileSplit192 = MfmaTile<128, 192, 32, 64, 96, 2, 8, 3>;
 // 192 x 128 blocks of 96 x 64 per wave.
-using TileTall = MfmaTile<192, 128, 16, 96, 64, 1, 8, 3>;
-using TileSmall = MfmaTile<64, 64, 16, 32, 32, 1, 4, 3>;
-// Three register sets carry its windows from global memory to LDS, so each
-// window's loads have three windows to arrive (1024^3: 23.9 -> 22.3 us).
+using TileTall = MfmaTile<192, 128, 16, 96, 64, 1, 8, 3, 1, 4, 8, 3>;
+using TileSmall = MfmaTile<64, 64, 16, 32, 32, 1, 4, 3, 1, 4, 8, 3>;
 using TileSplit64 = MfmaTile<64, 64, 32, 32, 32, 2, 4, 3, 1, 4, 8, 3>;
-// k split four ways: one 8-wide step per group and window, so two stages; two
-// register sets (512^3: 8.9 -> 8.7 us).
+// k split four ways: one 8-wide step per group and window, so two stages.
 using TileTiny = MfmaTile<32, 32, 32, 32, 32, 4, 4, 2, 1, 4, 8, 2>;
 // The same block with 64-wide windows and three stages: twice the work per
 // window and one more window in flight, for grids of at most one block per CU
 // over a long k, where TileTiny waits on its loads (512 x 512 x 32768: 352 ->
 // 230 us).  Its 57 KB of LDS allow two blocks per CU, so many-block grids stay
 // with TileTiny.
-using TileTiny64 = MfmaTile<32, 32, 64, 32, 32, 4, 4, 3>;
+using TileTiny64 = MfmaTile<32, 32, 64, 32, 32, 4, 4, 3, 1, 4, 8, 3>;
 
 constexpr int kTileCount = 8;
 

@@ -81,6 +81,37 @@ def test_tiles_all_layouts_exact(tile, layout):
                  exact=True)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lid)
+@pytest.mark.parametrize("tile", range(sg.sgemm_f32_mfma_tiles()), ids=sg.sgemm_f32_mfma_tile_name)
+def test_tiles_long_k_exact(tile, layout):
+    """Forty-one k windows (the last one partial) on a grid of nine blocks with
+    ragged edges: one round of blocks over a long k, where the configurations that
+    carry windows through a ring of register sets use it."""
+    bm, bn, bk = (int(x) for x in sg.sgemm_f32_mfma_tile_name(tile).split()[0].split("x"))
+    ta, tb = layout
+    M, N, K = 2 * bm + 37, 2 * bn + 19, 40 * bk + 3
+    As, Bs, C0 = _operands(M, N, K, "smallint", 650 + tile, ta, tb)
+    C = _run(As, Bs, M, N, K, ta, tb, 2.0, -1.0, C0, tile=tile)
+    check_ex(As, Bs, M, N, K, ta, tb, 2.0, -1.0, C0, C, f"tile {tile} {lid(layout)} long k",
+             exact=True)
+
+
+@pytest.mark.parametrize("layout", [(N_, N_), (T_, T_)], ids=lid)
+@pytest.mark.parametrize("tile", [4, 5], ids=sg.sgemm_f32_mfma_tile_name)
+def test_tiles_many_rounds_long_k_sampled(tile, layout):
+    """324 blocks (more than one per CU) over 101 k windows, the last one partial:
+    the register ring is used on grids of several rounds when k is this long."""
+    from gpu_helpers import sample_indices
+    bm, bn, bk = (int(x) for x in sg.sgemm_f32_mfma_tile_name(tile).split()[0].split("x"))
+    ta, tb = layout
+    M, N, K = 17 * bm + 5, 17 * bn + 5, 100 * bk + 7
+    As, Bs, C0 = _operands(M, N, K, "smallint", 660 + tile, ta, tb)
+    C = _run(As, Bs, M, N, K, ta, tb, 1.0, 1.0, C0, tile=tile)
+    r, c = sample_indices(M, N, rows=6, cols=6, elems=2048, seed=tile)
+    check_ex(As, Bs, M, N, K, ta, tb, 1.0, 1.0, C0, C, f"tile {tile} {lid(layout)} rounds",
+             exact=True, rows=r, cols=c)
+
+
 @pytest.mark.parametrize("algo", NN_ONLY + TRANS_ALGOS, ids=name)
 @pytest.mark.parametrize("shape", [(5, 300, 77), (300, 6, 77), (70, 90, 33)],
                          ids=lambda s: "x".join(map(str, s)))
