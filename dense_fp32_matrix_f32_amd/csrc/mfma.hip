@@ -20,10 +20,12 @@ namespace sgemm {
 // (window_floor_us below).  The four numbers per configuration were fitted
 // (least squares on log time) to timings of every configuration on 19 shapes on
 // MI355X, among them the 512^3, 1024^3, 2048 x 3072 x 4096, 4095 x 4097 x 1023
-// and 8192^3 products and four with a long k and few blocks; on 18 of them the
-// model picks the fastest configuration and on the other one within 0.2% of
-// it.  The smallest estimate wins.  The timings are of untransposed operands;
-// the other storage orders use the same choice.
+// and 8192^3 products and four with a long k and few blocks.  The fit predates
+// the register ring of the kernels; timed again with the ring, the model still
+// picks the fastest configuration on 16 of the 19 shapes and one within 1.5% of
+// it on the other three (4096^3, 16384 x 16384 x 1024, 256 x 8192 x 8192), so
+// the numbers were kept.  The smallest estimate wins.  The timings are of
+// untransposed operands; the other storage orders use the same choice.
 struct TileChoice {
     const char *name;  // block, k window, wave block, wave groups, LDS stages
     int bm, bn;
