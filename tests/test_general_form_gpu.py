@@ -96,6 +96,26 @@ def test_tiles_long_k_exact(tile, layout):
              exact=True)
 
 
+@pytest.mark.parametrize("layout", [(N_, N_), (T_, N_), (N_, T_)], ids=lid)
+@pytest.mark.parametrize("windows", [(16, 0), (17, 0), (18, 0), (17, 5), (19, 1)],
+                         ids=lambda w: f"w{w[0]}+{w[1]}")
+@pytest.mark.parametrize("tile", [1, 3, 4, 5, 6, 7], ids=sg.sgemm_f32_mfma_tile_name)
+def test_ring_window_counts_exact(tile, windows, layout):
+    """Every configuration with a register ring, on four blocks (one round) at the
+    smallest window counts that take the ring: 16, 17 and 18 whole windows leave
+    each possible number of steady windows (0, 1 or 2) after the last whole group
+    of two or three register sets, and a partial last window (k = 5 or 1 past the
+    whole ones) adds a guarded window to the tail."""
+    whole, extra = windows
+    bm, bn, bk = (int(x) for x in sg.sgemm_f32_mfma_tile_name(tile).split()[0].split("x"))
+    ta, tb = layout
+    M, N, K = bm + 5, bn + 3, whole * bk + extra
+    As, Bs, C0 = _operands(M, N, K, "smallint", 670 + tile + whole, ta, tb)
+    C = _run(As, Bs, M, N, K, ta, tb, 1.0, -2.0, C0, tile=tile)
+    check_ex(As, Bs, M, N, K, ta, tb, 1.0, -2.0, C0, C,
+             f"tile {tile} {lid(layout)} {whole} windows + {extra}", exact=True)
+
+
 @pytest.mark.parametrize("layout", [(N_, N_), (T_, T_)], ids=lid)
 @pytest.mark.parametrize("tile", [4, 5], ids=sg.sgemm_f32_mfma_tile_name)
 def test_tiles_many_rounds_long_k_sampled(tile, layout):
