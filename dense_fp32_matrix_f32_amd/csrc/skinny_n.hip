@@ -23,6 +23,12 @@ namespace sgemm {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int SKINNY_N_MAX_COLS = 8;
+// Values of k per LDS chunk of y (YM 5): 1024 for one column, 2048 for more
+// (sweeps of 512, 1024 and 2048 over 1 and 2 columns, 1023 to 8192 k).
+template <int NR>
+constexpr int skinny_n_chunk() {
+    return NR == 1 ? 1024 : 2048;
+}
 
 __device__ __forceinline__ f32x4 load16_n(const float *p) {
     f32x4 v;
@@ -39,7 +45,14 @@ __device__ __forceinline__ f32x4 load16_n(const float *p) {
 // row or the row padding of y and only feed outputs that are not stored; the
 // last four k rows, where that would read past the matrix, go value by value;
 // 4 (NR == N == 2, y dense: yk == 2, yj == 1) a lane's four rows are eight
-// consecutive floats, read as two 16-byte loads.
+// consecutive floats, read as two 16-byte loads; 5 (y's rows far apart, e.g. a
+// few columns of a wide B) chunks of skinny_n_chunk() values of k (all columns)
+// are gathered into LDS once per work-group, zero past K, and each lane
+// reads its four k of a column there as one 16-byte read.  Read value by value,
+// every wave touches one cache line per value of y (64 lines per load
+// instruction against 8 for its row of X); the gather does that once per
+// work-group.  The k order of every lane is the same in all modes, so the
+// results are too.
 template <int NR, int RW, int YM>
 __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                                                        const float *__restrict__ A, int64_t lda,
@@ -60,6 +73,7 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
 #pragma unroll
         for (int j = 0; j < NR; ++j) acc[r][j] = 0.0f;
 
+    if constexpr (YM != 5) {
     for (int k = 4 * lane; k < K; k += 256) {
         f32x4 a[RW];
         float b[4][NR];
@@ -140,6 +154,60 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                 acc[r][j] = fmaf(a[r].w, b[3][j], acc[r][j]);
             }
     }
+    } else {
+        // Work-item t gathers the values (k, j) of the chunk with k * NR + j = t +
+        // 256 i, so adjacent columns of one k come from adjacent work-items.  The
+        // gather completes before the chunk is used: the loads of X queue behind
+        // any load issued before them, and the gathered ones are slow.
+        constexpr int KC = skinny_n_chunk<NR>();  // k per chunk
+        constexpr int PER = NR * KC / 256;        // values gathered per work-item
+        static_assert(KC % 256 == 0, "a chunk holds whole 256-wide steps of the lanes");
+        __shared__ __attribute__((aligned(16))) float yl[NR * KC];
+        for (int k0 = 0; k0 < K; k0 += KC) {
+            if (k0 > 0) __syncthreads();  // the previous chunk has been read
+            float g[PER];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int u = threadIdx.x + 256 * i;
+                const int k = k0 + u / NR, j = u % NR;
+                g[i] = k < K ? B[(int64_t)k * yk + (int64_t)min(j, N - 1) * yj] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int u = threadIdx.x + 256 * i;
+                yl[(u % NR) * KC + u / NR] = g[i];
+            }
+            __syncthreads();
+            const int kend = min(K, k0 + KC);
+            for (int k = k0 + 4 * lane; k < kend; k += 256) {
+                f32x4 a[RW];
+                if (k + 3 < K) {
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) a[r] = load16_n(arow[r] + k);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) {
+                        a[r].x = arow[r][k];
+                        a[r].y = k + 1 < K ? arow[r][k + 1] : 0.0f;
+                        a[r].z = k + 2 < K ? arow[r][k + 2] : 0.0f;
+                        a[r].w = k + 3 < K ? arow[r][k + 3] : 0.0f;
+                    }
+                }
+                f32x4 b[NR];
+#pragma unroll
+                for (int j = 0; j < NR; ++j) b[j] = *(const f32x4 *)(yl + j * KC + (k - k0));
+#pragma unroll
+                for (int r = 0; r < RW; ++r)
+#pragma unroll
+                    for (int j = 0; j < NR; ++j) {
+                        acc[r][j] = fmaf(a[r].x, b[j].x, acc[r][j]);
+                        acc[r][j] = fmaf(a[r].y, b[j].y, acc[r][j]);
+                        acc[r][j] = fmaf(a[r].z, b[j].z, acc[r][j]);
+                        acc[r][j] = fmaf(a[r].w, b[j].w, acc[r][j]);
+                    }
+            }
+        }
+    }
 
     // Butterfly over the 64 lanes, the same pairing for every output.
 #pragma unroll
@@ -188,7 +256,8 @@ static hipError_t launch_cols(const ColStream &q, hipStream_t s) {
 // rows of 4096 k: two rows when y is read along k (YM 2) and for one column or
 // four whole columns (1.3 to 1.7 times faster than eight rows at 4096 rows); in
 // the other cases (y read value by value, or eight columns) the most rows that
-// still give 256 work-groups.
+// still give 256 work-groups (with y gathered into LDS, YM 5, one column kept
+// two rows: four or eight were up to 2% slower at 4096 and 16384 rows).
 template <int NR, int YM>
 static hipError_t launch_cols_rw(const ColStream &q, hipStream_t s) {
     const bool two = YM == 2 || YM == 4 || NR == 1 || (NR == 4 && (YM == 1 || YM == 3));
@@ -207,6 +276,11 @@ static hipError_t launch_cols_of(const ColStream &q, hipStream_t s) {
         if (q.yj == 1 && q.yk != 1 && q.yk + q.cols >= NR) return launch_cols_rw<NR, 3>(q, s);
     }
     if (q.yk == 1) return launch_cols_rw<NR, 2>(q, s);
+    // y's rows at least a cache line apart: gathered into LDS (with four or eight
+    // columns one of y's strides is 1, which the cases above take)
+    if constexpr (NR <= 2) {
+        if (q.K >= 256 && q.yk >= 32) return launch_cols_rw<NR, 5>(q, s);
+    }
     return launch_cols_rw<NR, 0>(q, s);
 }
 

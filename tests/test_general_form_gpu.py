@@ -132,6 +132,20 @@ def test_tiles_many_rounds_long_k_sampled(tile, layout):
              exact=True, rows=r, cols=c)
 
 
+@pytest.mark.parametrize("case", [(1, 3000, 1500, 39), (2, 777, 2049, 62), (1, 300, 4099, 31),
+                                  (2, 5000, 257, 98)], ids=lambda c: "x".join(map(str, c)))
+def test_few_rows_both_transposed_padded_a(case):
+    """One or two rows of C with both operands transposed: the few-rows rung runs
+    it as C^T = B^T op(A)^T on the few-columns kernel, with y = op(A)^T read from
+    the stored A, whose rows (lda = M + pad) are far apart: y is gathered into
+    LDS."""
+    M, N, K, pad = case
+    As, Bs, C0 = _operands(M, N, K, "smallint", 690 + K, T_, T_, pad_a=pad)
+    for algo in (sg.ALGO_AUTO, sg.ALGO_SKINNY):
+        C = _run(As, Bs, M, N, K, T_, T_, 3.0, -1.0, C0, algo)
+        check_ex(As, Bs, M, N, K, T_, T_, 3.0, -1.0, C0, C, f"{name(algo)} TT {case}", exact=True)
+
+
 @pytest.mark.parametrize("algo", NN_ONLY + TRANS_ALGOS, ids=name)
 @pytest.mark.parametrize("shape", [(5, 300, 77), (300, 6, 77), (70, 90, 33)],
                          ids=lambda s: "x".join(map(str, s)))

@@ -293,6 +293,26 @@ def test_few_columns(shape, algo):
     check_full(A, B, M, N, K, C, f"{name(algo)} {shape} padded B")
 
 
+# One or two columns of a wide B (rows of y at least a cache line apart): the
+# few-columns kernel gathers y into LDS per work-group, in chunks of k, zero past
+# K.  Several chunks with a partial last one, K not a multiple of 4, rows that do
+# not fill the last work-group, NaN in B's padding.
+WIDE_B = [(4095, 1, 1023, 4097), (777, 2, 2500, 64), (300, 1, 4099, 33), (1000, 2, 5000, 100),
+          (33, 1, 256, 32), (5000, 2, 2049, 4096), (257, 1, 300, 40), (8193, 2, 1999, 48)]
+
+
+@pytest.mark.parametrize("algo", [sg.ALGO_SKINNY_N, sg.ALGO_AUTO], ids=name)
+@pytest.mark.parametrize("case", WIDE_B, ids=lambda c: "x".join(map(str, c[:3])) + f"-ldb{c[3]}")
+def test_few_columns_of_wide_b(case, algo):
+    M, N, K, ldb = case
+    A, B = inputs(M, N, K, "smallint", seed=700 + M + K, ldb=ldb)
+    C = _run(A, B, M, N, K, algo)
+    check_full(A, B, M, N, K, C, f"{name(algo)} {case} int", exact=True)
+    A, B = inputs(M, N, K, "normal", seed=800 + M + K, lda=K + 3, ldb=ldb)
+    C = _run(A, B, M, N, K, algo, offset_elems=1)
+    check_full(A, B, M, N, K, C, f"{name(algo)} {case}")
+
+
 # ---------------------------------------------------------------- 64-bit offsets
 def _big_case(M, N, K, algo, rows=None, cols=None):
     """An operand of more than 2^31 elements, drawn on the device (seeded); the
