@@ -326,6 +326,49 @@ def timed_launches(torch, stream, launch, warm_ms=300.0, timed_ms=200.0, min_ste
     return [run(n) for _ in range(regions)], n * regions
 
 
+def launch_floor(torch, sg):
+    """Back-to-back time of the smallest launches: the fixed cost a product pays
+    whatever its size (under rocprofv3 --kernel-trace the kernels' own durations
+    come with it).  The tile ids are those of sgemm_f32_mfma_tile_name()."""
+    import statistics
+
+    stream = torch.cuda.current_stream()
+    n = 1 << 20
+    A = torch.randn(n, device="cuda")
+    B = torch.randn(n, device="cuda")
+    C = torch.empty(n, device="cuda")
+    t512 = sg.sgemm_f32_mfma_select(512, 512, 512)
+    t1024 = sg.sgemm_f32_mfma_select(1024, 1024, 1024)
+    bk512 = int(sg.sgemm_f32_mfma_tile_name(t512).split()[0].split("x")[2])
+    bk1024 = int(sg.sgemm_f32_mfma_tile_name(t1024).split()[0].split("x")[2])
+    cases = [("C = 0 (512 x 512, K = 0)", (512, 512, 0, None)), ("1 x 1 x 1", (1, 1, 1, None))]
+    for t, bk, m in ((t512, bk512, 512), (t1024, bk1024, 1024)):
+        bm = int(sg.sgemm_f32_mfma_tile_name(t).split("x")[0])
+        cases.append((f"tile {t}: one block, one window", (bm, bm, bk, t)))
+        cases.append((f"tile {t}: {m} x {m} x {bk}, one window per block", (m, m, bk, t)))
+        cases.append((f"tile {t}: {m} x {m} x {2 * bk}, two windows per block", (m, m, 2 * bk, t)))
+    for name, (M, N, K, tile) in cases:
+        lda = max(K, 1)
+        C[:1].zero_()  # a torch kernel between the cases marks their boundaries in a kernel trace
+
+        def launch():
+            if tile is None:
+                st = sg.sgemm_f32(M, N, K, A.data_ptr(), lda, B.data_ptr(), N, C.data_ptr(), N,
+                                  stream.cuda_stream)
+            else:
+                st = sg.sgemm_f32_mfma_tile(M, N, K, A.data_ptr(), lda, B.data_ptr(), N,
+                                            C.data_ptr(), N, stream.cuda_stream, tile)
+            if st != 0:
+                raise sg.SgemmError(st)
+
+        kms, launches = timed_launches(torch, stream, launch, warm_ms=50.0, timed_ms=50.0)
+        print(json.dumps({"launch": name, "shape": [M, N, K], "tile": tile,
+                          "us_median": round(statistics.median(kms) * 1e3, 3),
+                          "launches": launches,
+                          "timing": "one HIP event pair around each of 5 runs of back-to-back "
+                                    "launches"}), flush=True)
+
+
 def config_report(torch, sg, args):
     """One JSON line per workload: kernel time (median, mean, min of per-launch
     events), TFLOP/s and GB/s against the peaks, the algorithm and tile used; for
@@ -477,6 +520,9 @@ def main(argv=None):
     p.add_argument("--no-also", action="store_true", help="skip the 2048x3072x4096 product")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="CPU time budget of the oracle baseline (0 = skip)")
+    p.add_argument("--floor", action="store_true",
+                   help="time the smallest launches (K = 0, 1x1x1, one block and one k window of "
+                        "the small tiles, one window on 256 blocks) back to back, one JSON line each")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a device copy of known size (for HBM counter calibration)")
     p.add_argument("--ladder", action="store_true",
@@ -519,6 +565,9 @@ def main(argv=None):
         print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 3}), flush=True)
         return
 
+    if args.floor:
+        launch_floor(torch, sg)
+        return
     if args.configs:
         config_report(torch, sg, args)
         return
