@@ -8,7 +8,7 @@ few-columns streaming kernels, C = beta*C for K = 0, accumulation into C
 (beta = 1), and split-k through a workspace.  The graph is replayed several times with eager work and
 synchronizations in between (the operands change between replays); every replay
 is compared with the oracle, bitwise on small-integer data.  A second test runs
-products on two streams at once.
+products on two streams at once, a third from four host threads at once.
 """
 import numpy as np
 import pytest
@@ -119,3 +119,55 @@ def test_concurrent_streams():
             got = out.cpu().numpy()
             g = got if rows is None else got[rows, cols]
             assert np.array_equal(g.astype(np.float64), want), (M, N, K)
+
+
+def test_host_threads():
+    """Four host threads call the library at once, each on its own stream with its
+    own outputs and workspace: blocks of the matrix cores, the few-rows kernel, a
+    product with an edge strip, and split-k through a workspace."""
+    import threading
+
+    torch = torch_cuda()
+    shapes = [(700, 900, 650), (1, 4096, 1500), (2049, 4097, 300), (128, 96, 20000)]
+    inputs = []
+    for i, (M, N, K) in enumerate(shapes):
+        A = synthgen.matrix(M, K, seed=140 + i, stream=0, dist="smallint")
+        B = synthgen.matrix(K, N, seed=140 + i, stream=1, dist="smallint")
+        inputs.append((M, N, K, A, B, torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()))
+    threads_n = 4
+    streams = [torch.cuda.Stream() for _ in range(threads_n)]
+    outs = [[torch.full((M, N), float("nan"), device="cuda") for (M, N, K, *_) in inputs]
+            for _ in range(threads_n)]
+    ws_bytes = [sg.sgemm_f32_workspace_size(0, 0, M, N, K) for (M, N, K, *_) in inputs]
+    assert ws_bytes[-1] > 0, "the last shape should split k"
+    wss = [torch.empty(max(ws_bytes) // 4 + 1, device="cuda") for _ in range(threads_n)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            for rep in range(10):
+                for j, (M, N, K, A, B, dA, dB) in enumerate(inputs):
+                    st = sg.sgemm_f32_ex_ws(0, 0, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N,
+                                            0.0, outs[t][j].data_ptr(), N, wss[t].data_ptr(),
+                                            ws_bytes[j], streams[t].cuda_stream)
+                    if st != 0:
+                        errors.append((t, j, st))
+        except Exception as e:  # reported below, on the main thread
+            errors.append((t, repr(e)))
+
+    log(f"[gpu] {threads_n} host threads")
+    pool = [threading.Thread(target=worker, args=(t,)) for t in range(threads_n)]
+    for th in pool:
+        th.start()
+    for th in pool:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for j, (M, N, K, A, B, dA, dB) in enumerate(inputs):
+        rows, cols = _elements(M, N, j)
+        want = _exact(A, B, 0.0, None, rows, cols)
+        for t in range(threads_n):
+            got = outs[t][j].cpu().numpy()
+            g = got if rows is None else got[rows, cols]
+            assert np.array_equal(g.astype(np.float64), want), (t, M, N, K)
