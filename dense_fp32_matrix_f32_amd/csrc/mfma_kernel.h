@@ -194,31 +194,37 @@ template <class T, bool TA_, bool TB_, bool NARROW_ = true, int RING_ = T::RING>
 struct Cfg : T {
     static constexpr bool TA = TA_, TB = TB_, NARROW = NARROW_;
     static constexpr int RING = RING_;  // register sets used by this instantiation
-    // B as given whose lanes hold three adjacent columns (96-wide wave blocks) is
-    // copied in 12-byte pieces, one per lane's three columns, each into a 16-byte
-    // slot of its LDS row (the fourth float is zero and never read into an MFMA),
-    // so a fragment is one aligned 16-byte read instead of an 8-byte and a 4-byte
-    // one (2048 x 3072 x 4096: 142.1 -> 143.6 TFLOP/s, B transposed as the first
-    // operand: 139.3 -> 140.9).  The same form for A transposed with 96-high wave
-    // blocks measured 1.2-1.4% slower on the 192 x 128 block, so A keeps 16-byte
-    // copies.
-    static constexpr bool B3 = !TB && T::TN == 3;
+    // B as given whose lanes hold three adjacent columns (96-wide wave blocks).
+    // With A as given it is copied in 12-byte pieces, one per lane's three
+    // columns, each into a 16-byte slot of its LDS row (the fourth float is zero
+    // and never read into an MFMA), so a fragment is one aligned 16-byte read
+    // instead of an 8-byte and a 4-byte one (B3; 2048 x 3072 x 4096: 142.1 ->
+    // 143.6 TFLOP/s).  With A transposed it is loaded as 16-byte pieces of its
+    // rows and written to LDS along k, as a transposed B is (BX): three 16-byte
+    // fragment reads per step instead of four (365.1 -> 360.0 us at 2048 x 3072 x
+    // 4096; with A as given the two forms measured within 0.2%).  The fragments
+    // and the stores of C follow B's LDS layout (BKC).  The 12-byte form for A
+    // transposed with 96-high wave blocks measured 1.2-1.4% slower on the 192 x
+    // 128 block, so A keeps 16-byte copies.
+    static constexpr bool B3 = !TA && !TB && T::TN == 3;
+    static constexpr bool BX = TA && !TB && T::TN == 3;
+    static constexpr bool BKC = TB || BX;  // B's LDS window: k-contiguous rows per column
     static constexpr int AW = 4, BW = B3 ? 3 : 4;           // floats per copied vector
     static constexpr int B_ROW = B3 ? T::BN / 3 * 4 : T::BN;  // LDS floats per B row
     static constexpr int PA = TA ? T::BM + T::PAD_B : T::BK + T::PAD_A;  // A window pitch
-    static constexpr int PB = TB ? T::BK + T::PAD_A : B_ROW + T::PAD_B;  // B window pitch
+    static constexpr int PB = BKC ? T::BK + T::PAD_A : B_ROW + T::PAD_B;  // B window pitch
     static constexpr int A_STAGE = (TA ? T::BK : T::BM) * PA;
-    static constexpr int B_STAGE = (TB ? T::BN : T::BK) * PB;
+    static constexpr int B_STAGE = (BKC ? T::BN : T::BK) * PB;
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int LDS_FLOATS = T::STAGES * STAGE > T::RED ? T::STAGES * STAGE : T::RED;
     // Copied vectors per window and per work-item.
     static constexpr int A_TOTAL = T::BM * T::BK / AW, B_TOTAL = T::BK * T::BN / BW;
     static constexpr int A_VECS = (A_TOTAL + T::THREADS - 1) / T::THREADS;
     static constexpr int B_VECS = (B_TOTAL + T::THREADS - 1) / T::THREADS;
-    static constexpr int DSW = A_VECS + B_VECS;  // LDS writes per window
+    static constexpr int DSW = A_VECS + (BX ? 4 : 1) * B_VECS;  // LDS writes per window
     static constexpr int VMR = A_VECS + B_VECS;  // global loads per window
     static constexpr int DSR_A = TA ? 4 * lds_reads(T::TM) : T::TM;  // LDS reads per step
-    static constexpr int DSR_B = TB ? T::TN : 4 * (B3 ? 1 : lds_reads(T::TN));
+    static constexpr int DSR_B = BKC ? T::TN : 4 * (B3 ? 1 : lds_reads(T::TN));
     static constexpr int DSR = DSR_A + DSR_B;
     // The steady-state loop writes LDS in the first step of a window and issues
     // the `vmr` global loads of a later window in the same step, or in the second
@@ -228,6 +234,8 @@ struct Cfg : T {
         return (T::STEPS > 1 && T::MF < DSR + DSW + vmr) ? 1 : 0;
     }
     static_assert(!B3 || T::BN % 3 == 0, "three-wide B rows");
+    static_assert(!BX || (T::BK % 16 == 0 && T::BN % 16 == 0 && B_TOTAL % 64 == 0),
+                  "B written along k: 16 rows by 4 vectors per wave");
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 };
 
@@ -254,7 +262,7 @@ using Acc = f32x16[T::TM][T::TN];
 //     floats; rows beyond `extent` read the last valid one.
 //   mn-contiguous (W = 4 or 3): BK rows of COLS floats (along m or n); columns
 //     beyond `extent` read the last valid one.
-template <class T, bool KC, int ROWS_OR_COLS, int TOTAL, int VECS, int W = 4>
+template <class T, bool KC, int ROWS_OR_COLS, int TOTAL, int VECS, int W = 4, bool XP = false>
 struct Operand {
     static_assert(W == 4 || (W == 3 && !KC), "three-float vectors along m or n only");
     static constexpr int Q = KC ? T::BK / 4 : ROWS_OR_COLS / W;  // vectors per LDS row
@@ -264,6 +272,7 @@ struct Operand {
     int lds[VECS];
     int kofs[VECS];  // KC: k offset of the vector in the window; else its k row
     int pos[VECS];   // mn-contiguous: first column (m or n) of the vector
+    int pitch_;      // LDS pitch (XP: between columns)
     f32x4 r[VECS];
 
     __device__ __forceinline__ static bool has(int tid, int v) {
@@ -279,7 +288,15 @@ struct Operand {
     // 16-byte LDS stores).  Each work-item still loads a whole 16-byte vector and
     // each wave the same 64-byte row pieces.
     __device__ __forceinline__ static void place(int c, int &row, int &q) {
-        if constexpr (KC && Q == 4 && TOTAL % 64 == 0 && T::BK + T::PAD_A == 20) {
+        if constexpr (XP) {
+            // mn-contiguous window written along k: each wave loads 16 rows by 4
+            // vectors (64 bytes of each row); its 4-byte LDS stores of one column
+            // offset e then land in 64 different banks (pitch BK + 4 = 36 floats)
+            const int l = c & 63, chunk = c >> 6;
+            constexpr int KB = T::BK / 16;
+            row = 16 * (chunk % KB) + (l >> 2);
+            q = 4 * (chunk / KB) + (l & 3);
+        } else if constexpr (KC && Q == 4 && TOTAL % 64 == 0 && T::BK + T::PAD_A == 20) {
             const int l = c & 63;
             row = (c >> 6) * 16 + ((l >> 2) & 3) * 4 + (l >> 4);
             q = l & 3;
@@ -312,8 +329,10 @@ struct Operand {
                 kofs[v] = row;
                 pos[v] = origin + q * W;
             }
-            lds[v] = base + row * pitch + q * 4;
+            // XP: column q*W + e of the window at k = row, in rows of BK per column
+            lds[v] = XP ? base + q * W * pitch + row : base + row * pitch + q * 4;
         }
+        pitch_ = pitch;
     }
 
     // Start of vector v in window 0.
@@ -390,7 +409,16 @@ struct Operand {
     __device__ __forceinline__ void stash(float *stage, int tid) const {
 #pragma unroll
         for (int v = 0; v < VECS; ++v)
-            if (has(tid, v)) *(f32x4 *)(stage + lds[v]) = r[v];
+            if (has(tid, v)) {
+                if constexpr (XP) {
+                    stage[lds[v]] = r[v].x;
+                    stage[lds[v] + pitch_] = r[v].y;
+                    stage[lds[v] + 2 * pitch_] = r[v].z;
+                    stage[lds[v] + 3 * pitch_] = r[v].w;
+                } else {
+                    *(f32x4 *)(stage + lds[v]) = r[v];
+                }
+            }
     }
 };
 
@@ -415,7 +443,7 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
     const int wm = sw / C::WAVES_N, wn = sw % C::WAVES_N;
 
     Operand<C, !C::TA, C::BM, C::A_TOTAL, C::A_VECS, C::AW> a;
-    Operand<C, C::TB, C::BN, C::B_TOTAL, C::B_VECS, C::BW> b;
+    Operand<C, C::TB, C::BN, C::B_TOTAL, C::B_VECS, C::BW, C::BX> b;
     a.init(g.A, lda, m0, M, 0, C::PA, tid);
     b.init(g.B, ldb, n0, N, C::A_STAGE, C::PB, tid);
     // mn-contiguous blocks that reach past their matrix read clamped columns
@@ -436,14 +464,14 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
     // Fragment placement (see the header comment).
     const int a_frag = C::TA ? (4 * lh) * C::PA + wm * C::WM + C::TM * lr
                              : (wm * C::WM + lr) * C::PA + 4 * lh;
-    const int b_frag = C::A_STAGE + (C::TB ? (wn * C::WN + lr) * C::PB + 4 * lh
+    const int b_frag = C::A_STAGE + (C::BKC ? (wn * C::WN + lr) * C::PB + 4 * lh
                                            : (4 * lh) * C::PB + (C::B3 ? (wn * C::WN / 3 + lr) * 4
                                                                        : wn * C::WN + C::TN * lr));
 
     // Fragments of one 8-wide k step.
     struct Frag {
         typename std::conditional<C::TA, AVec[4], f32x4[C::TM]>::type a;
-        typename std::conditional<C::TB, f32x4[C::TN], BVec[4]>::type b;
+        typename std::conditional<C::BKC, f32x4[C::TN], BVec[4]>::type b;
     };
     auto read_frag = [&](Frag &f, const float *s, int t) {
         const int k8 = (t * C::KW + kg) * 8;
@@ -455,7 +483,7 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
             for (int i = 0; i < C::TM; ++i)
                 f.a[i] = *(const f32x4 *)(s + a_frag + i * 32 * C::PA + k8);
         }
-        if constexpr (C::TB) {
+        if constexpr (C::BKC) {
 #pragma unroll
             for (int j = 0; j < C::TN; ++j)
                 f.b[j] = *(const f32x4 *)(s + b_frag + j * 32 * C::PB + k8);
@@ -477,7 +505,7 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
                     } else {
                         av = f.a[i][q];
                     }
-                    if constexpr (C::TB) {
+                    if constexpr (C::BKC) {
                         bv = f.b[j][q];
                     } else {
                         bv = lane_of<BL>(f.b[q], j);
@@ -828,8 +856,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
         return strip_m + (C::TA ? C::TM * rho + i : 32 * i + rho);
     };
     // mn-contiguous B: a lane's TN adjacent columns; k-contiguous B: one column per block
-    const int col0 = strip_n + (C::TB ? lr : C::TN * lr);
-    auto col_of = [&](int j) { return col0 + (C::TB ? 32 * j : j); };
+    const int col0 = strip_n + (C::BKC ? lr : C::TN * lr);
+    auto col_of = [&](int j) { return col0 + (C::BKC ? 32 * j : j); };
     auto put = [&](float *dst, float v) { *dst = epilogue(v, alpha, beta, dst); };
     // mn-contiguous B: the lane's TN adjacent columns of row r of block row i as one
     // access (read-modify-write when beta != 0).
@@ -855,7 +883,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
             for (int r = 0; r < 16; ++r) {
                 if (!mine(r)) continue;
                 float *dst = Cm + (int64_t)row_of(i, r) * ldc;
-                if constexpr (!C::TB) {
+                if constexpr (!C::BKC) {
                     put_row(dst, i, r);
                 } else {
 #pragma unroll
@@ -871,7 +899,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
         // block past M only, such as the last block row of a 4095-row product,
         // then stores as fast as the others: all blocks finish together, so one
         // slow epilogue delays them all).
-        const bool row_inside = !C::TB && col0 >= n_lo && col0 + C::TN <= N;
+        const bool row_inside = !C::BKC && col0 >= n_lo && col0 + C::TN <= N;
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
@@ -880,7 +908,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, int m0, int n0, co
                 if (mine(r) && row >= m_lo && row < M) {
                     float *dst = Cm + (int64_t)row * ldc;
                     if (row_inside) {
-                        if constexpr (!C::TB) put_row(dst, i, r);
+                        if constexpr (!C::BKC) put_row(dst, i, r);
                     } else {
 #pragma unroll
                         for (int j = 0; j < C::TN; ++j)
