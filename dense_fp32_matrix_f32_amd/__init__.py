@@ -70,7 +70,10 @@ def matmul(A, B, out=None, algo="auto", stream=None, alpha=1.0, beta=0.0, worksp
     "auto", ``workspace`` (a contiguous CUDA tensor, or "auto" to allocate the
     size sgemm_f32_workspace_size asks for through torch) lets products with few
     blocks of C split k across work-groups.  The product is enqueued on
-    ``stream`` (default: torch's current stream) without synchronising."""
+    ``stream`` (default: torch's current stream) without synchronising; tensors
+    allocated here (``out`` when None, the "auto" workspace) are marked as used on
+    that stream, so torch's allocator does not hand their memory out again before
+    the product has finished there."""
     import torch
     pa, lda, ta = _operand(A, "A")
     pb, ldb, tb = _operand(B, "B")
@@ -78,10 +81,12 @@ def matmul(A, B, out=None, algo="auto", stream=None, alpha=1.0, beta=0.0, worksp
     K2, N = B.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    made = []  # tensors allocated here, to be marked as used on the launch stream
     if out is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs out")
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        made.append(out)
     elif tuple(out.shape) != (M, N):
         raise ValueError("out has the wrong shape")
     pc, ldc, tc = _operand(out, "out")
@@ -96,6 +101,7 @@ def matmul(A, B, out=None, algo="auto", stream=None, alpha=1.0, beta=0.0, worksp
                     raise ValueError('workspace must be a tensor, "auto" or None')
                 nbytes = sgemm_f32_workspace_size(int(ta), int(tb), M, N, K)
                 workspace = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=A.device)
+                made.append(workspace)
             if not workspace.is_cuda or not workspace.is_contiguous():
                 raise ValueError("workspace must be a contiguous CUDA tensor")
             st = sgemm_f32_ex_ws(int(ta), int(tb), M, N, K, float(alpha), pa, lda, pb, ldb,
@@ -106,4 +112,7 @@ def matmul(A, B, out=None, algo="auto", stream=None, alpha=1.0, beta=0.0, worksp
                                    float(beta), pc, ldc, s.cuda_stream, algo_id)
     if st != 0:
         raise SgemmError(st)
+    if isinstance(s, torch.cuda.Stream):
+        for t in made:
+            t.record_stream(s)
     return out

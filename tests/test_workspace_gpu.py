@@ -91,6 +91,18 @@ def test_matmul_helper_workspace():
         C = sg.matmul(At, Bt, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(C.cpu().numpy().astype(np.float64), want)
+    # on a side stream: the workspace and C that matmul allocates are released as
+    # soon as it returns, while the product may still run there; new allocations
+    # on the current stream, filled at once, must not land on them
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        C = sg.matmul(At, Bt, workspace="auto", stream=side)
+        junk = [torch.full((1 << 20,), float("nan"), device="cuda") for _ in range(4)]
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), want), rep
+        del junk
 
 
 def _reduce_groups(M, N, slices):
