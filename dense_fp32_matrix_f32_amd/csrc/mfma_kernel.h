@@ -233,6 +233,15 @@ struct Cfg : T {
     static constexpr int load_step(int vmr) {
         return (T::STEPS > 1 && T::MF < DSR + DSW + vmr) ? 1 : 0;
     }
+    // The 128 x 128 wave blocks (one wave per SIMD, two steps per window) with A
+    // as given issue the loads of A (64-byte row pieces, 16 rows per instruction)
+    // in the first step, with the LDS stores, and those of B in the second,
+    // instead of all of them in the first: 4095 x 4097 x 1023 263.9 -> 257.1 us,
+    // 8192^3 (B as given or transposed) and 4096^3 0.3-0.4% faster.  With A
+    // transposed the split was neutral to 0.5% slower, and on the 128 x 128 block
+    // (four 32 x 128 waves) 0.7-0.8% slower at 16384 x 16384 x 1024 and 6000 x
+    // 6000 x 1000.
+    static constexpr bool SPLIT_LOADS = T::STEPS == 2 && T::TM == 4 && T::TN == 4 && !TA;
     static_assert(!B3 || T::BN % 3 == 0, "three-wide B rows");
     static_assert(!BX || (T::BK % 16 == 0 && T::BN % 16 == 0 && B_TOTAL % 64 == 0),
                   "B written along k: 16 rows by 4 vectors per wave");
@@ -579,7 +588,11 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
                         read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
                     }
                     if (t == 0) stash(fill);
-                    if (t == LOAD_STEP) {
+                    if constexpr (C::SPLIT_LOADS) {
+                        const int64_t k0 = (int64_t)(w + C::STAGES) * C::BK;
+                        if (t == 0) a.template fetch_full<!EDGE>(k0, lda, M);
+                        if (t == 1) b.template fetch_full<!EDGE>(k0, ldb, N);
+                    } else if (t == LOAD_STEP) {
                         const int64_t k0 = (int64_t)(w + C::STAGES) * C::BK;
                         a.template fetch_full<!EDGE>(k0, lda, M);
                         b.template fetch_full<!EDGE>(k0, ldb, N);
@@ -590,7 +603,13 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
                     constexpr int RL = C::STAGES == 3 ? C::DSR : 0;
                     constexpr int R1 = 2 < C::STEPS ? C::DSR : RL;
                     constexpr int VM0 = LOAD_STEP == 0 ? VMR : 0;
-                    if (t == 0) {
+                    constexpr int VMA = EDGE ? (C::TA ? 4 : 1) * C::A_VECS : C::A_VECS;
+                    constexpr int VMB = VMR - VMA;
+                    if (C::SPLIT_LOADS && t == 0) {
+                        interleave<C::MF, R0, C::DSW, VMA>();
+                    } else if (C::SPLIT_LOADS) {
+                        interleave<C::MF, RL, 0, VMB>();
+                    } else if (t == 0) {
                         interleave<C::MF, R0, C::DSW, VM0>();
                     } else if (t == LOAD_STEP) {
                         interleave<C::MF, R1, 0, VMR>();
