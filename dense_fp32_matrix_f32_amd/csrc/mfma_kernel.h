@@ -238,9 +238,10 @@ struct Cfg : T {
     // in the first step, with the LDS stores, and those of B in the second,
     // instead of all of them in the first: 4095 x 4097 x 1023 263.9 -> 257.1 us,
     // 8192^3 (B as given or transposed) and 4096^3 0.3-0.4% faster.  With A
-    // transposed the split was neutral to 0.5% slower, and on the 128 x 128 block
+    // transposed the split was neutral to 0.5% slower, on the 128 x 128 block
     // (four 32 x 128 waves) 0.7-0.8% slower at 16384 x 16384 x 1024 and 6000 x
-    // 6000 x 1000.
+    // 6000 x 1000, on the 128 x 192 block 0.5% slower at 2048 x 3072 x 4096, and
+    // on the 192 x 128 block neutral.
     static constexpr bool SPLIT_LOADS = T::STEPS == 2 && T::TM == 4 && T::TN == 4 && !TA;
     static_assert(!B3 || T::BN % 3 == 0, "three-wide B rows");
     static_assert(!BX || (T::BK % 16 == 0 && T::BN % 16 == 0 && B_TOTAL % 64 == 0),
