@@ -50,6 +50,9 @@ static_assert(sizeof(kTiles) / sizeof(kTiles[0]) == kTileCount, "one entry per c
 static_assert(kTiles[0].bm == TileHuge::BM && kTiles[0].bn == TileHuge::BN, "row 0");
 static_assert(kTiles[1].bm == TileWide::BM && kTiles[1].bn == TileWide::BN, "row 1");
 static_assert(kTiles[2].bm == TileSplit192::BM && kTiles[2].bn == TileSplit192::BN, "row 2");
+static_assert(TileWide192::BM == TileSplit192::BM && TileWide192::BN == TileSplit192::BN &&
+                  TileWide192::BK == TileSplit192::BK,
+              "row 2 in both wave shapes");
 static_assert(kTiles[3].bm == TileTall::BM && kTiles[3].bn == TileTall::BN, "row 3");
 static_assert(kTiles[4].bm == TileSmall::BM && kTiles[4].bn == TileSmall::BN, "row 4");
 static_assert(kTiles[5].bm == TileSplit64::BM && kTiles[5].bn == TileSplit64::BN, "row 5");

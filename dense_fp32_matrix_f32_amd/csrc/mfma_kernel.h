@@ -1179,6 +1179,17 @@ using TileWide = MfmaTile<128, 128, 16, 32, 128, 1, 8, 3, 1, 4, 8, 3>;
 // 128 x 192 blocks of 64 x 96 per wave, k split over two wave groups (two waves
 // per SIMD): one block per CU on grids of about 256 blocks, such as 2048 x 3072.
 using TileSplit192 = MfmaTile<128, 192, 32, 64, 96, 2, 8, 3>;
+// The same block as eight waves of 32 x 96 without the k split (two waves per
+// SIMD), in its place when only B is transposed: B's fragments are then one
+// 16-byte read per 32-wide block, and 2048 x 3072 x 4096 ran at 146.2 against
+// 144.5 TFLOP/s, other shapes on this block 1.0-3.1% faster.  With B as given
+// the two measured within 0.3% at 2048 x 3072 x 4096 and 2000 x 3001 x 4000
+// (1.6% faster at 1999 x 2999 x 1000; TileSplit192 kept); with A transposed a
+// 32-high wave reads A one float per k and was 1.7% (B transposed too) and 4.2%
+// slower.
+using TileWide192 = MfmaTile<128, 192, 32, 32, 96, 1, 8, 3>;
+template <bool TA, bool TB>
+using Tile192 = typename std::conditional<!TA && TB, TileWide192, TileSplit192>::type;
 // 192 x 128 blocks of 96 x 64 per wave.
 using TileTall = MfmaTile<192, 128, 16, 96, 64, 1, 8, 3, 1, 4, 8, 3>;
 using TileSmall = MfmaTile<64, 64, 16, 32, 32, 1, 4, 3, 1, 4, 8, 3>;
@@ -1212,7 +1223,7 @@ hipError_t launch_mfma_tt_splitk(const Problem &p, hipStream_t s, int tile, int 
         switch (tile) {                                                                       \
         case 0: return launch_tile<TileHuge, TA, TB>(p, s);                                   \
         case 1: return launch_tile<TileWide, TA, TB>(p, s);                                   \
-        case 2: return launch_tile<TileSplit192, TA, TB>(p, s);                               \
+        case 2: return launch_tile<Tile192<TA, TB>, TA, TB>(p, s);                            \
         case 3: return launch_tile<TileTall, TA, TB>(p, s);                                   \
         case 4: return launch_tile<TileSmall, TA, TB>(p, s);                                  \
         case 5: return launch_tile<TileSplit64, TA, TB>(p, s);                                \

@@ -225,7 +225,10 @@ hipError_t sgemm_f32_colmajor(int transa, int transb, int M, int N, int K, float
  * sgemm_f32_mfma_tiles()      number of configurations (ids 0 .. count-1).
  * sgemm_f32_mfma_tile_name()  static description such as
  *                             "256x256x16 w128x128 k1 s3" (BM x BN x BK, wave
- *                             block, wave groups, stages); NULL for an unknown id.
+ *                             block, wave groups, stages; the 128 x 192
+ *                             configuration runs eight 32 x 96 waves in one
+ *                             group instead when B alone is transposed); NULL
+ *                             for an unknown id.
  * sgemm_f32_mfma_select()     the id SGEMM_F32_ALGO_MFMA uses for an M x N x K
  *                             product on a device with `compute_units` CUs
  *                             (<= 0 means 256); host-only, no HIP call; -1 if
