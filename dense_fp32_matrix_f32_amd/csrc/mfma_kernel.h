@@ -108,21 +108,22 @@ __device__ __forceinline__ f32x4 load16_at(const char *base, uint32_t off) {
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// 12-byte loads into the first three lanes of a vector whose fourth is zero:
-// from a 4-byte aligned address, and through a buffer resource as load16_at.
+// 12-byte loads into the first three lanes of a vector whose fourth is left
+// undefined (it is never used): from a 4-byte aligned address, and through a
+// buffer resource as load16_at.
+typedef float f32x3 __attribute__((ext_vector_type(3)));
+
 __device__ __forceinline__ f32x4 load12(const float *p) {
-    f32x4 v;
-    __builtin_memcpy(&v, p, 12);
-    v.w = 0.0f;
-    return v;
+    f32x3 x;
+    __builtin_memcpy(&x, p, 12);
+    return __builtin_shufflevector(x, x, 0, 1, 2, -1);
 }
 
 __device__ __forceinline__ f32x4 load12_at(const char *base, uint32_t off) {
-    typedef float f32x3 __attribute__((ext_vector_type(3)));
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, -1, 0x00020000);
     const f32x3 x = __builtin_bit_cast(f32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0));
-    return f32x4{x.x, x.y, x.z, 0.0f};
+    return __builtin_shufflevector(x, x, 0, 1, 2, -1);
 }
 
 // Scheduling hint for one basic block holding MF MFMAs, DSR LDS reads, DSW LDS
@@ -196,9 +197,9 @@ struct Cfg : T {
     static constexpr int RING = RING_;  // register sets used by this instantiation
     // B as given whose lanes hold three adjacent columns (96-wide wave blocks).
     // With A as given it is copied in 12-byte pieces, one per lane's three
-    // columns, each into a 16-byte slot of its LDS row (the fourth float is zero
-    // and never read into an MFMA), so a fragment is one aligned 16-byte read
-    // instead of an 8-byte and a 4-byte one (B3; 2048 x 3072 x 4096: 142.1 ->
+    // columns, each into a 16-byte slot of its LDS row (the fourth float is
+    // undefined and never read into an MFMA), so a fragment is one aligned 16-byte
+    // read instead of an 8-byte and a 4-byte one (B3; 2048 x 3072 x 4096: 142.1 ->
     // 143.6 TFLOP/s).  With A transposed it is loaded as 16-byte pieces of its
     // rows and written to LDS along k, as a transposed B is (BX): three 16-byte
     // fragment reads per step instead of four (365.1 -> 360.0 us at 2048 x 3072 x
@@ -267,7 +268,8 @@ using Acc = f32x16[T::TM][T::TN];
 // Global -> register -> LDS copy of one operand's k window, for the `VECS`
 // vectors of W floats this work-item owns (vector v exists iff tid + v*THREADS <
 // TOTAL; a missing one re-reads the last vector and is not stored).  Each vector
-// lands in a 16-byte slot of LDS (W = 3: the fourth float is zero).
+// lands in a 16-byte slot of LDS (W = 3: the fourth float is undefined and is
+// never read into an MFMA).
 //   k-contiguous (KC, W = 4): ROWS rows (of op(A) or columns of op(B)) of BK
 //     floats; rows beyond `extent` read the last valid one.
 //   mn-contiguous (W = 4 or 3): BK rows of COLS floats (along m or n); columns
@@ -288,6 +290,12 @@ struct Operand {
     __device__ __forceinline__ static bool has(int tid, int v) {
         return (TOTAL % T::THREADS == 0) || tid + v * T::THREADS < TOTAL;
     }
+
+    // Every work-item owns every one of its vectors and vector v lies THREADS/Q
+    // rows after vector 0 (both placements below keep q and add THREADS/Q to the
+    // row): its LDS slot is a fixed distance after vector 0's, so a window's
+    // stores need one address and immediate offsets.
+    static constexpr bool LINEAR = !XP && TOTAL % T::THREADS == 0 && T::THREADS % Q == 0;
 
     // Vector c of the window -> its row and its vector q within the row.  A
     // k-contiguous window of four vectors per row (16-wide k windows, rows padded
@@ -420,13 +428,18 @@ struct Operand {
 #pragma unroll
         for (int v = 0; v < VECS; ++v)
             if (has(tid, v)) {
+                const int at = LINEAR ? lds[0] + v * (T::THREADS / Q) * pitch_ : lds[v];
                 if constexpr (XP) {
                     stage[lds[v]] = r[v].x;
                     stage[lds[v] + pitch_] = r[v].y;
                     stage[lds[v] + 2 * pitch_] = r[v].z;
                     stage[lds[v] + 3 * pitch_] = r[v].w;
+                } else if constexpr (W == 3) {
+                    // the first three floats of the 16-byte slot (one 12-byte store)
+                    typedef float f32x3s __attribute__((ext_vector_type(3), aligned(16)));
+                    *(f32x3s *)(stage + at) = f32x3s{r[v].x, r[v].y, r[v].z};
                 } else {
-                    *(f32x4 *)(stage + lds[v]) = r[v];
+                    *(f32x4 *)(stage + at) = r[v];
                 }
             }
     }
