@@ -468,7 +468,7 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
     Operand<C, !C::TA, C::BM, C::A_TOTAL, C::A_VECS, C::AW> a;
     Operand<C, C::TB, C::BN, C::B_TOTAL, C::B_VECS, C::BW, C::BX> b;
     a.init(g.A, lda, m0, M, 0, C::PA, tid);
-    b.init(g.B, ldb, n0, N, C::A_STAGE, C::PB, tid);
+    b.init(g.B, ldb, n0, N, 0, C::PB, tid);
     // mn-contiguous blocks that reach past their matrix read clamped columns
     const bool a_inside = !C::TA || m0 + C::BM <= M;
     const bool b_inside = C::TB || n0 + C::BN <= N;
@@ -478,41 +478,46 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
         a.fetch(k0, lda, M, K, a_inside);
         b.fetch(k0, ldb, N, K, b_inside);
     };
+    // LDS holds the STAGES windows of A, then the STAGES windows of B.  With a
+    // stage index known at compile time every LDS address in the loop is one
+    // register per operand plus an immediate offset.
+    auto a_stage = [&](int stage) { return lds + stage * C::A_STAGE; };
+    auto b_stage = [&](int stage) { return lds + C::STAGES * C::A_STAGE + stage * C::B_STAGE; };
     auto stash = [&](int stage) {
-        float *s = lds + stage * C::STAGE;
-        a.stash(s, tid);
-        b.stash(s, tid);
+        a.stash(a_stage(stage), tid);
+        b.stash(b_stage(stage), tid);
     };
 
     // Fragment placement (see the header comment).
     const int a_frag = C::TA ? (4 * lh) * C::PA + wm * C::WM + C::TM * lr
                              : (wm * C::WM + lr) * C::PA + 4 * lh;
-    const int b_frag = C::A_STAGE + (C::BKC ? (wn * C::WN + lr) * C::PB + 4 * lh
-                                           : (4 * lh) * C::PB + (C::B3 ? (wn * C::WN / 3 + lr) * 4
-                                                                       : wn * C::WN + C::TN * lr));
+    const int b_frag = C::BKC ? (wn * C::WN + lr) * C::PB + 4 * lh
+                              : (4 * lh) * C::PB + (C::B3 ? (wn * C::WN / 3 + lr) * 4
+                                                          : wn * C::WN + C::TN * lr);
 
     // Fragments of one 8-wide k step.
     struct Frag {
         typename std::conditional<C::TA, AVec[4], f32x4[C::TM]>::type a;
         typename std::conditional<C::BKC, f32x4[C::TN], BVec[4]>::type b;
     };
-    auto read_frag = [&](Frag &f, const float *s, int t) {
+    auto read_frag = [&](Frag &f, int stage, int t) {
+        const float *sa = a_stage(stage), *sb = b_stage(stage);
         const int k8 = (t * C::KW + kg) * 8;
         if constexpr (C::TA) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) f.a[q] = *(const AVec *)(s + a_frag + (k8 + q) * C::PA);
+            for (int q = 0; q < 4; ++q) f.a[q] = *(const AVec *)(sa + a_frag + (k8 + q) * C::PA);
         } else {
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
-                f.a[i] = *(const f32x4 *)(s + a_frag + i * 32 * C::PA + k8);
+                f.a[i] = *(const f32x4 *)(sa + a_frag + i * 32 * C::PA + k8);
         }
         if constexpr (C::BKC) {
 #pragma unroll
             for (int j = 0; j < C::TN; ++j)
-                f.b[j] = *(const f32x4 *)(s + b_frag + j * 32 * C::PB + k8);
+                f.b[j] = *(const f32x4 *)(sb + b_frag + j * 32 * C::PB + k8);
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) f.b[q] = *(const BVec *)(s + b_frag + (k8 + q) * C::PB);
+            for (int q = 0; q < 4; ++q) f.b[q] = *(const BVec *)(sb + b_frag + (k8 + q) * C::PB);
         }
     };
     auto multiply = [&](const Frag &f) {
@@ -555,9 +560,8 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
             if constexpr (C::STAGES == 3) {
                 if (w_begin + 2 < w_end) fetch((int64_t)(w_begin + 2) * C::BK);
                 if (second) {
-                    float *s1 = lds + C::STAGE;
-                    a1.stash(s1, tid);
-                    b1.stash(s1, tid);
+                    a1.stash(a_stage(1), tid);
+                    b1.stash(b_stage(1), tid);
                 }
             } else {
                 if (second) {
@@ -573,7 +577,7 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
         Frag frag[2];
         int cur = 0;  // LDS stage of window w
         int w = w_begin;
-        if constexpr (C::STAGES == 3) read_frag(frag[0], lds, 0);
+        if constexpr (C::STAGES == 3) read_frag(frag[0], 0, 0);
 
         // Steady state: a window whose successors up to w + STAGES are all full.
         // The body has no branches, so the copies of later windows (LDS stores of
@@ -589,25 +593,26 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
                                      : C::VMR;
             constexpr int LOAD_STEP = C::load_step(VMR);
             const int steady_end = min(w_end, K / C::BK) - C::STAGES;
-            for (; w < steady_end; ++w) {
-                const float *s = lds + cur * C::STAGE;
-                const int next = cur + 1 == C::STAGES ? 0 : cur + 1;
-                const int fill = cur == 0 ? C::STAGES - 1 : cur - 1;
-                if constexpr (C::STAGES == 2) read_frag(frag[0], s, 0);
+            // Window wi in LDS stage `stage` (a compile-time constant, or an int).
+            auto window = [&](auto stage, int wi) {
+                const int cs = stage;
+                const int next = cs + 1 == C::STAGES ? 0 : cs + 1;
+                const int fill = cs == 0 ? C::STAGES - 1 : cs - 1;
+                if constexpr (C::STAGES == 2) read_frag(frag[0], cs, 0);
     #pragma unroll
                 for (int t = 0; t < C::STEPS; ++t) {
                     if (t + 1 < C::STEPS) {
-                        read_frag(frag[(t + 1) & 1], s, t + 1);
+                        read_frag(frag[(t + 1) & 1], cs, t + 1);
                     } else if constexpr (C::STAGES == 3) {
-                        read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
+                        read_frag(frag[(t + 1) & 1], next, 0);
                     }
                     if (t == 0) stash(fill);
                     if constexpr (C::SPLIT_LOADS) {
-                        const int64_t k0 = (int64_t)(w + C::STAGES) * C::BK;
+                        const int64_t k0 = (int64_t)(wi + C::STAGES) * C::BK;
                         if (t == 0) a.template fetch_full<!EDGE>(k0, lda, M);
                         if (t == 1) b.template fetch_full<!EDGE>(k0, ldb, N);
                     } else if (t == LOAD_STEP) {
-                        const int64_t k0 = (int64_t)(w + C::STAGES) * C::BK;
+                        const int64_t k0 = (int64_t)(wi + C::STAGES) * C::BK;
                         a.template fetch_full<!EDGE>(k0, lda, M);
                         b.template fetch_full<!EDGE>(k0, ldb, N);
                     }
@@ -635,7 +640,20 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 __syncthreads();
-                cur = next;
+            };
+            // Groups of STAGES windows begin and end in stage 0, so the stage of
+            // every window in them is a constant (interior blocks; edge blocks
+            // keep the loop below, whose clamped loads need more registers).
+            if (!EDGE && cur == 0) {
+                for (; w + C::STAGES <= steady_end; w += C::STAGES) {
+                    window(std::integral_constant<int, 0>{}, w);
+                    window(std::integral_constant<int, 1>{}, w + 1);
+                    if constexpr (C::STAGES == 3) window(std::integral_constant<int, 2>{}, w + 2);
+                }
+            }
+            for (; w < steady_end; ++w) {
+                window(cur, w);
+                cur = cur + 1 == C::STAGES ? 0 : cur + 1;
             }
         };
         if (interior) {
@@ -647,18 +665,17 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
         // Remaining windows (the last STAGES ones and a partial last window): the
         // same schedule with the copies guarded.
         for (; w < w_end; ++w) {
-            const float *s = lds + cur * C::STAGE;
             const int next = cur + 1 == C::STAGES ? 0 : cur + 1;
-            if constexpr (C::STAGES == 2) read_frag(frag[0], s, 0);
+            if constexpr (C::STAGES == 2) read_frag(frag[0], cur, 0);
     #pragma unroll
             for (int t = 0; t < C::STEPS; ++t) {
                 // Issue the reads of the following step before this step's MFMAs.  After
                 // the last window the cross-window read fetches an unused stage; keeping
                 // it unconditional lets the LDS wait counts stay exact.
                 if (t + 1 < C::STEPS) {
-                    read_frag(frag[(t + 1) & 1], s, t + 1);
+                    read_frag(frag[(t + 1) & 1], cur, t + 1);
                 } else if constexpr (C::STAGES == 3) {
-                    read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
+                    read_frag(frag[(t + 1) & 1], next, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 multiply(frag[t & 1]);
@@ -716,9 +733,8 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
 #pragma unroll
             for (int j = 0; j < S - 1; ++j) {
                 if (j < n) {
-                    float *st = lds + j * C::STAGE;
-                    pa[j].stash(st, tid);
-                    pb[j].stash(st, tid);
+                    pa[j].stash(a_stage(j), tid);
+                    pb[j].stash(b_stage(j), tid);
                 }
             }
         }
@@ -726,7 +742,7 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
 
         Frag frag[2];
         int cur = 0;  // LDS stage of the current window
-        if constexpr (S == 3) read_frag(frag[0], lds, 0);
+        if constexpr (S == 3) read_frag(frag[0], 0, 0);
         // Windows whose ring loads (window i + S - 1 + R) are full windows run the
         // branch-free schedule; the rest guard their stores and loads.
         const int steady_n = min(n, K / C::BK - w_begin) - S - R + 1;
@@ -738,22 +754,21 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
             constexpr int VMR = EDGE ? (C::TA ? 4 : 1) * C::A_VECS + (C::TB ? 1 : C::BW) * C::B_VECS
                                      : C::VMR;
             constexpr int LOAD_STEP = C::load_step(VMR);
-            const float *sp = lds + cur * C::STAGE;
             const int next = cur + 1 == S ? 0 : cur + 1;
             const int fill = cur == 0 ? S - 1 : cur - 1;
-            float *fill_stage = lds + fill * C::STAGE;
-            if constexpr (S == 2) read_frag(frag[0], sp, 0);
+            float *fill_a = a_stage(fill), *fill_b = b_stage(fill);
+            if constexpr (S == 2) read_frag(frag[0], cur, 0);
 #pragma unroll
             for (int t = 0; t < C::STEPS; ++t) {
                 if (t + 1 < C::STEPS) {
-                    read_frag(frag[(t + 1) & 1], sp, t + 1);
+                    read_frag(frag[(t + 1) & 1], cur, t + 1);
                 } else if constexpr (S == 3) {
-                    read_frag(frag[(t + 1) & 1], lds + next * C::STAGE, 0);
+                    read_frag(frag[(t + 1) & 1], next, 0);
                 }
                 if constexpr (STEADY) {
                     if (t == 0) {
-                        as[Q].stash(fill_stage, tid);
-                        bs[Q].stash(fill_stage, tid);
+                        as[Q].stash(fill_a, tid);
+                        bs[Q].stash(fill_b, tid);
                     }
                     if (t == LOAD_STEP) {
                         const int64_t k0 = win_k0(i + S - 1 + R);
@@ -783,8 +798,8 @@ __device__ __forceinline__ void mma_tile(const GemmArgs &g, float *lds, int m0, 
             }
             if constexpr (!STEADY) {
                 if (i + S - 1 < n) {
-                    as[Q].stash(fill_stage, tid);
-                    bs[Q].stash(fill_stage, tid);
+                    as[Q].stash(fill_a, tid);
+                    bs[Q].stash(fill_b, tid);
                     if (i + S - 1 + R < n) {
                         as[Q].fetch(win_k0(i + S - 1 + R), lda, M, K, a_inside);
                         bs[Q].fetch(win_k0(i + S - 1 + R), ldb, N, K, b_inside);
