@@ -21,9 +21,10 @@ namespace sgemm {
 // (least squares on log time) to timings of every configuration on 19 shapes on
 // MI355X, among them the 512^3, 1024^3, 2048 x 3072 x 4096, 4095 x 4097 x 1023
 // and 8192^3 products and four with a long k and few blocks.  The fit predates
-// the register ring of the kernels; timed again with the ring, the model still
-// picks the fastest configuration on 16 of the 19 shapes and one within 1.5% of
-// it on the other three (4096^3, 16384 x 16384 x 1024, 256 x 8192 x 8192), so
+// the register ring of the kernels and their stage-unrolled loops; timed again
+// on the current kernels, the model picks the fastest configuration on 15 of the
+// 19 shapes and one within 2.4% of it on the other four (4095 x 4097 x 1023 over
+// the whole shape, 4096 x 4096 x 256, 256 x 8192 x 8192, 8192 x 256 x 8192), so
 // the numbers were kept.  The smallest estimate wins.  The timings are of
 // untransposed operands; the other storage orders use the same choice.
 struct TileChoice {
