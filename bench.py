@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -67,11 +68,21 @@ def tile_intensity(tm: int, tn: int) -> float:
     return 2 * tm * tn / ((tm + tn) * 4)
 
 
+def code_tokens(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed, so that a
+    change to comments or layout alone leaves the hash below unchanged (string
+    literals in these files hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code of the kernel sources (comments and whitespace ignored)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

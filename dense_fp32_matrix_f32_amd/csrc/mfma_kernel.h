@@ -17,6 +17,11 @@
 //   * the operand fragments of the next 8-wide k step are read from LDS while
 //     the MFMAs of the current step run; with three stages this reaches across
 //     the window boundary, so the barrier does not leave the matrix cores idle;
+//   * LDS holds the stages of A, then those of B; the steady loop runs groups
+//     of STAGES windows whose stages are compile-time constants, so each LDS
+//     access is one register per operand plus an immediate offset and the loop
+//     issues no vector instructions for addresses (a vector instruction between
+//     MFMAs costs the matrix core several cycles);
 //   * each wave owns a WM x WN sub-block held as (WM/32) x (WN/32) accumulators
 //     of v_mfma_f32_32x32x2f32 (full fp32 inputs, fp32 accumulation, 4096 flops
 //     per instruction), which is where the per-element fused multiply-adds of
