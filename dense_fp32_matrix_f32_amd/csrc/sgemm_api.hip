@@ -165,9 +165,10 @@ hipError_t launch_auto_mfma(const Problem &p, hipStream_t s) {
 // long k leave most CUs idle (128 x 128 x 65536: 4 blocks of 64 x 64); they split
 // k into slices whose unscaled partial products go to workspace planes, added by
 // a second kernel in an order fixed by the shape (deterministic, no atomics).
-// The few-rows kernel was tried the same way (512-byte row segments, 16 slices
-// for 1 x 4096 x 4096) and lost to the plain kernel by the second launch, so it
-// never splits.
+// The few-rows kernel was tried the same way (row segments of 512 bytes to 4 KiB
+// for 1 x 4096 x 4096): the partial sums alone read B as fast as a contiguous
+// copy, but adding them, by a second launch or by the last group to arrive,
+// costs more than the strips lose, so it never splits.
 enum WsKind { WS_NONE = 0, WS_MFMA = 1 };
 struct WsPlan {
     int kind, tile, slices;
