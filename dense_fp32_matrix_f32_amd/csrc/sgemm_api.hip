@@ -11,14 +11,20 @@ using sgemm::Problem;
 
 namespace {
 
-// Byte extent [lo, hi) of a rows x cols row-major array with row stride ld.
+// Byte extent [lo, hi) of a rows x cols row-major array with row stride ld
+// (rows, cols, ld >= 1).  Sizes near the int range make the byte count exceed
+// 64 bits, so it is formed in 128 bits and hi saturates at the top of the
+// address space rather than wrapping below lo.
 struct Extent {
     uintptr_t lo, hi;
 };
 
 Extent extent(const void *p, int64_t rows, int64_t cols, int64_t ld) {
     const uintptr_t lo = (uintptr_t)p;
-    return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * (int64_t)sizeof(float))};
+    const unsigned __int128 bytes =
+        ((unsigned __int128)(uint64_t)(rows - 1) * (uint64_t)ld + (uint64_t)cols) * sizeof(float);
+    const unsigned __int128 hi = (unsigned __int128)lo + bytes;
+    return {lo, hi > (unsigned __int128)UINTPTR_MAX ? UINTPTR_MAX : (uintptr_t)hi};
 }
 
 bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }

@@ -66,6 +66,16 @@ def test_invalid_arguments_rejected_before_any_hip_call(args):
                                base["B"], base["ldb"], base["C"], base["ldc"]) == -1
 
 
+def test_overlap_found_when_the_byte_extent_passes_64_bits():
+    # A of 2^31 - 1 rows with a row stride of 2^31 - 1 floats spans almost 2^64
+    # bytes; starting at 2^62 its end lies past the top of the address space.  C
+    # starts inside it, so the call is refused (a wrapped end would hide that).
+    big = 2**31 - 1
+    a = 1 << 62
+    st = sg.sgemm_f32(big, 1, 1, a, big, B_ADDR, 1, a + 4096, 1, 0)
+    assert st == INVALID, st
+
+
 def test_unknown_algorithm_rejected():
     assert sg.sgemm_f32_algo(8, 8, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR, 8, 0, 17) == INVALID
     assert sg.sgemm_f32_algo(8, 8, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR, 8, 0, -1) == INVALID
