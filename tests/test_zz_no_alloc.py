@@ -101,3 +101,66 @@ def test_noalloc_without_split_and_beyond_scratch():
     st, C = _call("noalloc", torch, dA, dB, C0, M, N, K, N_, N_, 1.0, 0.0)
     assert st == HIP_ERROR_INVALID_VALUE, f"expected hipErrorInvalidValue, got {st}"
     assert np.all(C == 3.0)
+
+
+def test_noalloc_captured_in_a_graph():
+    """Calls recorded under HIP graph capture (the callers the entry point is for):
+    two split products whose planes share the static array, and one without a
+    split, all accumulating into C.  The graph is replayed three times; between
+    replays an eager split call of another shape overwrites the array and the
+    operands change.  Every replay is checked bitwise against the oracle on small
+    integers."""
+    torch = torch_cuda()
+    shapes = [(128, 96, 20000, N_, N_), (200, 150, 9000, T_, N_), (300, 200, 100, N_, T_)]
+    cases = []
+    for i, (M, N, K, ta, tb) in enumerate(shapes):
+        torch, As, Bs, C0, dA, dB = _case(M, N, K, ta, tb, "smallint", 970 + i)
+        dC = torch.from_numpy(C0.copy()).cuda()
+        cases.append(dict(M=M, N=N, K=K, ta=ta, tb=tb, As=As, Bs=Bs, C0=C0, dA=dA, dB=dB, dC=dC))
+    assert sg.sgemm_f32_workspace_size(N_, N_, 128, 96, 20000) > 0
+    assert sg.sgemm_f32_workspace_size(T_, N_, 200, 150, 9000) > 0
+    assert sg.sgemm_f32_workspace_size(N_, T_, 300, 200, 100) == 0
+    # another split shape, run eagerly between replays (the array's address on
+    # this device is looked up by the first call, made here before the capture)
+    eA = torch.from_numpy(synthgen.matrix(512, 32768, seed=980, stream=0, dist="smallint")).cuda()
+    eB = torch.from_numpy(synthgen.matrix(32768, 512, seed=980, stream=1, dist="smallint")).cuda()
+    eC = torch.empty((512, 512), dtype=torch.float32, device="cuda")
+
+    def eager_split():
+        st = sg.sgemm_f32_ex_noalloc(N_, N_, 512, 512, 32768, 1.0, eA.data_ptr(), 32768,
+                                     eB.data_ptr(), 512, 0.0, eC.data_ptr(), 512,
+                                     torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+
+    def call(c, s):
+        M, N, K, ta, tb = c["M"], c["N"], c["K"], c["ta"], c["tb"]
+        return sg.sgemm_f32_ex_noalloc(ta, tb, M, N, K, 1.0, c["dA"].data_ptr(),
+                                       M if ta else K, c["dB"].data_ptr(), K if tb else N,
+                                       1.0, c["dC"].data_ptr(), N, s)
+
+    eager_split()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        s = torch.cuda.current_stream().cuda_stream
+        for c in cases:
+            assert call(c, s) == 0
+    for replay in range(3):
+        log(f"[gpu] noalloc graph replay {replay}")
+        graph.replay()
+        torch.cuda.synchronize()
+        for c in cases:
+            got = c["dC"].cpu().numpy()
+            want, _ = oracle.sgemm_ex(c["As"], c["Bs"], c["ta"], c["tb"], 1.0, 1.0, c["C0"])
+            assert np.array_equal(got.astype(np.float64), want), \
+                (c["M"], c["N"], c["K"], replay)
+            c["C0"] = got
+            # eager work between replays: new operands for the next replay
+            c["dA"].mul_(-1.0)
+            c["As"] = c["dA"].cpu().numpy()
+        eager_split()
+        torch.cuda.synchronize()
+    r, c = sample_indices(512, 512, rows=4, cols=4, elems=2048, seed=7)
+    want, _ = oracle.sgemm_ex(eA.cpu().numpy(), eB.cpu().numpy(), 0, 0, 1.0, 0.0,
+                              np.zeros((512, 512), np.float32), rows=r, cols=c)
+    assert np.array_equal(eC.cpu().numpy()[r, c].astype(np.float64), want)
