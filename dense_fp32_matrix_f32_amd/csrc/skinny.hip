@@ -5,9 +5,11 @@
 // the chip's ridge point: the product is bound by reading B once from HBM.  The
 // kernel therefore streams B exactly once with 16-byte loads, keeps up to 8 rows
 // of A in flight per element of B, and splits K across the work-items of a
-// work-group (k = slot, slot + S, slot + 2S, ...), followed by a reduction over
-// the slots in a fixed order (across the lanes of each wave, then the waves in
-// LDS), so results are reproducible and no atomics are needed.  Each work-group owns a strip of 4*LPR columns; with 16 columns (64
+// work-group, followed by a reduction over the slots in a fixed order (across
+// the lanes of each wave, then the waves in LDS), so results are reproducible and
+// no atomics are needed.  With x contiguous along k, slot s takes runs of four
+// consecutive k (4s .. 4s+3, then 4s + 4S .. 4s + 4S + 3, ...), so each run of x
+// is one 16-byte load; with x strided along k it takes k = s, s + S, s + 2S, ...  Each work-group owns a strip of 4*LPR columns; with 16 columns (64
 // bytes of a row) two work-groups share every 128-byte line, so strips are
 // assigned XCD by XCD: neighbouring strips run on the same XCD and a line comes
 // through its L2 once, not once per XCD.
@@ -105,6 +107,41 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
                 acc[m][3] = fmaf(a[m], b.w, acc[m][3]);
             }
         };
+        if constexpr (XK1) {
+            // One run of four consecutive k per step: four loads of B and one
+            // 16-byte load per row of x in flight.  Measured against 16 single k
+            // per batch (rows slot + u*S) with B streamed from HBM: 1 x 4096 x 4096
+            // 18.3 -> 17.0 us, 2 to 4 rows 3-5% and 8 rows 6% faster, 1 x 4097 x
+            // 1023 (resident) 5.7 -> 4.3 us; more runs per step, or pairs, were no
+            // faster, and some were twice as slow.
+            int k = 4 * slot;
+            for (; k + 3 < K; k += 4 * S) {
+                f32x4 b[4];
+                f32x4 a[MR];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = load_b(k + j);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) a[m] = load16_skinny(arow[m] + k);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float av[MR];
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) av[m] = a[m][j];
+                    fma4(av, b[j]);
+                }
+            }
+            // the last run of a slot, cut by K
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                if (k + j < K) {
+                    const f32x4 bv = load_b(k + j);
+                    float av[MR];
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) av[m] = arow[m][k + j];
+                    fma4(av, bv);
+                }
+            return;
+        }
         int k = slot;
         for (; k + (U - 1) * S < K; k += U * S) {
             f32x4 b[U];
@@ -211,14 +248,31 @@ static hipError_t launch_rows(const RowStream &q, hipStream_t s) {
                   q.beta);
 }
 
+template <int MR>
+static hipError_t launch_rows_k1(const RowStream &q, hipStream_t s) {
+    // x contiguous along k (runs of four k per slot): 512 work-items while the
+    // strips give at most one work-group per CU, else 256 (measured on 1 to 8
+    // rows of 1024 to 16384 columns, B resident and streamed from HBM).
+    const int64_t groups = q.cols >= 64 * 256 ? (q.cols + 63) / 64 : (q.cols + 15) / 16;
+    if (groups <= compute_units()) return launch_rows<MR, 512, true>(q, s);
+    return launch_rows<MR, 256, true>(q, s);
+}
+
 template <bool XK1>
 static hipError_t launch_rows_of(const RowStream &q, hipStream_t s) {
-    // Group sizes measured on 1..8 x 4096 x 4096 with B resident in the
-    // Infinity Cache and streamed from HBM.
-    if (q.rows == 1) return launch_rows<1, 256, XK1>(q, s);
-    if (q.rows == 2) return launch_rows<2, 512, XK1>(q, s);
-    if (q.rows <= 4) return launch_rows<4, 512, XK1>(q, s);
-    return launch_rows<8, 256, XK1>(q, s);
+    if constexpr (XK1) {
+        if (q.rows == 1) return launch_rows_k1<1>(q, s);
+        if (q.rows == 2) return launch_rows_k1<2>(q, s);
+        if (q.rows <= 4) return launch_rows_k1<4>(q, s);
+        return launch_rows_k1<8>(q, s);
+    } else {
+        // Group sizes measured on 1..8 x 4096 x 4096 with B resident in the
+        // Infinity Cache and streamed from HBM.
+        if (q.rows == 1) return launch_rows<1, 256, false>(q, s);
+        if (q.rows == 2) return launch_rows<2, 512, false>(q, s);
+        if (q.rows <= 4) return launch_rows<4, 512, false>(q, s);
+        return launch_rows<8, 256, false>(q, s);
+    }
 }
 
 static hipError_t launch_row_stream(const RowStream &p, hipStream_t s) {
