@@ -605,9 +605,8 @@ def main(argv=None):
             dBs.append(torch.from_numpy(synthgen.matrix(N if tb_ else K, K if tb_ else N,
                                                         seed=args.seed + 100 + r, stream=1,
                                                         dist=args.dist)).cuda())
-    chosen = sg.sgemm_f32_select(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N)
-    if layout != (0, 0):
-        chosen = sg.ALGO_MFMA
+    # the algorithm the automatic choice takes for this shape and storage order
+    chosen, _, _ = sg.sgemm_f32_auto_plan(layout[0], layout[1], M, N, K)
     used = chosen if algo == sg.ALGO_AUTO else algo
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up, algo "
           f"{sg.sgemm_f32_algo_name(used)}", file=sys.stderr, flush=True)

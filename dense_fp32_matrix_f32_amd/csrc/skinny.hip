@@ -109,11 +109,12 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(
         };
         if constexpr (XK1) {
             // One run of four consecutive k per step: four loads of B and one
-            // 16-byte load per row of x in flight.  Measured against 16 single k
-            // per batch (rows slot + u*S) with B streamed from HBM: 1 x 4096 x 4096
-            // 18.3 -> 17.0 us, 2 to 4 rows 3-5% and 8 rows 6% faster, 1 x 4097 x
-            // 1023 (resident) 5.7 -> 4.3 us; more runs per step, or pairs, were no
-            // faster, and some were twice as slow.
+            // 16-byte load per row of x in flight.  Against 16 single k per batch
+            // (rows slot + u*S), back-to-back launches on the same box, B streamed
+            // from HBM: 1 x 4096 x 4096 18.5 -> 17.6-17.8 us, 2 rows 18.6 -> 18.4,
+            // 8 rows 22.4 -> 21.4, 1 x 8192 x 8192 68.3 -> 64.6; B resident: 1 x
+            // 4096 x 4096 13.5 -> 13.0 us, 8 rows 15.3 -> 16.1.  More runs per
+            // step, or pairs, were no faster, and some were twice as slow.
             int k = 4 * slot;
             for (; k + 3 < K; k += 4 * S) {
                 f32x4 b[4];

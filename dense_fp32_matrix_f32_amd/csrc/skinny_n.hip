@@ -52,8 +52,9 @@ __device__ __forceinline__ f32x4 load16_n(const float *p) {
 // every wave touches one cache line per value of y (64 lines per load
 // instruction against 8 for its row of X); the gather does that once per
 // work-group.  The k order of every lane is the same in all modes, so the
-// results are too.
-template <int NR, int RW, int YM>
+// results are too.  U: steps of 256 k whose loads of X (and of y, when read
+// from memory) are all issued before any of them is used.
+template <int NR, int RW, int YM, int U = 1>
 __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                                                        const float *__restrict__ A, int64_t lda,
                                                        const float *__restrict__ B, int64_t yk,
@@ -73,11 +74,8 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
 #pragma unroll
         for (int j = 0; j < NR; ++j) acc[r][j] = 0.0f;
 
-    if constexpr (YM != 5) {
-    for (int k = 4 * lane; k < K; k += 256) {
-        f32x4 a[RW];
-        float b[4][NR];
-        if (k + 3 < K) {
+    // The four k from k on (k + 3 < K) of the lane's rows of X and of y.
+    auto load_full = [&](int k, f32x4 (&a)[RW], float (&b)[4][NR]) {
 #pragma unroll
             for (int r = 0; r < RW; ++r) a[r] = load16_n(arow[r] + k);
             if constexpr (YM == 1 || YM == 3) {
@@ -128,6 +126,37 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                     for (int j = 0; j < NR; ++j)
                         b[e][j] = B[(int64_t)(k + e) * yk + (int64_t)min(j, N - 1) * yj];
             }
+    };
+    auto fma_step = [&](const f32x4 (&a)[RW], const float (&b)[4][NR]) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                acc[r][j] = fmaf(a[r].x, b[0][j], acc[r][j]);
+                acc[r][j] = fmaf(a[r].y, b[1][j], acc[r][j]);
+                acc[r][j] = fmaf(a[r].z, b[2][j], acc[r][j]);
+                acc[r][j] = fmaf(a[r].w, b[3][j], acc[r][j]);
+            }
+    };
+
+    if constexpr (YM != 5) {
+    int k = 4 * lane;
+    if constexpr (U > 1) {
+        // whole batches of U steps
+        for (; k + 256 * (U - 1) + 3 < K; k += 256 * U) {
+            f32x4 a[U][RW];
+            float b[U][4][NR];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_full(k + 256 * u, a[u], b[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) fma_step(a[u], b[u]);
+        }
+    }
+    for (; k < K; k += 256) {
+        f32x4 a[RW];
+        float b[4][NR];
+        if (k + 3 < K) {
+            load_full(k, a, b);
         } else {
             // Last partial piece of the row: terms with k >= K are zero.
 #pragma unroll
@@ -144,15 +173,7 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                     b[e][j] = k + e < K ? B[(int64_t)(k + e) * yk + (int64_t)min(j, N - 1) * yj]
                                         : 0.0f;
         }
-#pragma unroll
-        for (int r = 0; r < RW; ++r)
-#pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                acc[r][j] = fmaf(a[r].x, b[0][j], acc[r][j]);
-                acc[r][j] = fmaf(a[r].y, b[1][j], acc[r][j]);
-                acc[r][j] = fmaf(a[r].z, b[2][j], acc[r][j]);
-                acc[r][j] = fmaf(a[r].w, b[3][j], acc[r][j]);
-            }
+        fma_step(a, b);
     }
     } else {
         // Work-item t gathers the values (k, j) of the chunk with k * NR + j = t +
@@ -179,7 +200,33 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
             }
             __syncthreads();
             const int kend = min(K, k0 + KC);
-            for (int k = k0 + 4 * lane; k < kend; k += 256) {
+            int k = k0 + 4 * lane;
+            if constexpr (U > 1) {
+                for (; k + 256 * (U - 1) + 3 < kend; k += 256 * U) {
+                    f32x4 a[U][RW];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+#pragma unroll
+                        for (int r = 0; r < RW; ++r) a[u][r] = load16_n(arow[r] + k + 256 * u);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        f32x4 b[NR];
+#pragma unroll
+                        for (int j = 0; j < NR; ++j)
+                            b[j] = *(const f32x4 *)(yl + j * KC + (k + 256 * u - k0));
+#pragma unroll
+                        for (int r = 0; r < RW; ++r)
+#pragma unroll
+                            for (int j = 0; j < NR; ++j) {
+                                acc[r][j] = fmaf(a[u][r].x, b[j].x, acc[r][j]);
+                                acc[r][j] = fmaf(a[u][r].y, b[j].y, acc[r][j]);
+                                acc[r][j] = fmaf(a[u][r].z, b[j].z, acc[r][j]);
+                                acc[r][j] = fmaf(a[u][r].w, b[j].w, acc[r][j]);
+                            }
+                    }
+                }
+            }
+            for (; k < kend; k += 256) {
                 f32x4 a[RW];
                 if (k + 3 < K) {
 #pragma unroll
@@ -243,12 +290,32 @@ struct ColStream {
     float alpha, beta;
 };
 
-template <int NR, int RW, int YM>
-static hipError_t launch_cols(const ColStream &q, hipStream_t s) {
+template <int NR, int RW, int YM, int U>
+static hipError_t launch_cols_u(const ColStream &q, hipStream_t s) {
     const int64_t groups = (q.rows + 4 * RW - 1) / (4 * RW);
     if (groups > INT32_MAX) return hipErrorInvalidValue;
-    return launch(skinny_n_kernel<NR, RW, YM>, dim3((unsigned)groups), dim3(256), 0, s, q.rows,
+    return launch(skinny_n_kernel<NR, RW, YM, U>, dim3((unsigned)groups), dim3(256), 0, s, q.rows,
                   q.cols, q.K, q.X, q.ldx, q.y, q.yk, q.yj, q.out, q.ci, q.cj, q.alpha, q.beta);
+}
+
+// Steps per batch.  With y read along k (YM 2), two dense columns (YM 4) or y
+// gathered into LDS (YM 5), two rows per wave and at most four columns: eight
+// steps of 256 k per batch when K >= 2048 (four with four columns, or when a
+// chunk of y holds only four), four when K is shorter, one step at a time
+// otherwise.  Against one step at a time (back-to-back launches, the same box):
+// 4096 x 1 x 4096 11.9 -> 11.4 us, 2048 x 1 x 16384 30.7 -> 25.0 us, a row times
+// a transposed 4096 x 4096 matrix streamed from HBM 14.9 -> 13.9 us, 4096 x 2 x
+// 4096 and the last column of 4095 x 4097 x 1023 level.  The other modes load
+// more values of y per step and keep one step at a time.
+template <int NR, int RW, int YM>
+static hipError_t launch_cols(const ColStream &q, hipStream_t s) {
+    constexpr bool BATCH = RW == 2 && (YM == 2 || YM == 4 || YM == 5) && NR <= 4;
+    if constexpr (BATCH) {
+        constexpr int UMAX = NR == 4 ? 4 : YM == 5 ? skinny_n_chunk<NR>() / 256 : 8;
+        if (UMAX >= 8 && q.K >= 2048) return launch_cols_u<NR, RW, YM, (UMAX >= 8 ? 8 : 1)>(q, s);
+        if (q.K > 768) return launch_cols_u<NR, RW, YM, 4>(q, s);  // four steps per lane
+    }
+    return launch_cols_u<NR, RW, YM, 1>(q, s);
 }
 
 // Rows per wave.  More rows re-use each value of y more often; fewer give more
