@@ -52,8 +52,8 @@ __device__ __forceinline__ f32x4 load16_n(const float *p) {
 // every wave touches one cache line per value of y (64 lines per load
 // instruction against 8 for its row of X); the gather does that once per
 // work-group.  The k order of every lane is the same in all modes, so the
-// results are too.  U: steps of 256 k whose loads of X (and of y, when read
-// from memory) are all issued before any of them is used.
+// results are too.  U (y read from memory): steps of 256 k whose loads are all
+// issued before any of them is used.
 template <int NR, int RW, int YM, int U = 1>
 __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
                                                        const float *__restrict__ A, int64_t lda,
@@ -200,33 +200,7 @@ __global__ __launch_bounds__(256) void skinny_n_kernel(int M, int N, int K,
             }
             __syncthreads();
             const int kend = min(K, k0 + KC);
-            int k = k0 + 4 * lane;
-            if constexpr (U > 1) {
-                for (; k + 256 * (U - 1) + 3 < kend; k += 256 * U) {
-                    f32x4 a[U][RW];
-#pragma unroll
-                    for (int u = 0; u < U; ++u)
-#pragma unroll
-                        for (int r = 0; r < RW; ++r) a[u][r] = load16_n(arow[r] + k + 256 * u);
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        f32x4 b[NR];
-#pragma unroll
-                        for (int j = 0; j < NR; ++j)
-                            b[j] = *(const f32x4 *)(yl + j * KC + (k + 256 * u - k0));
-#pragma unroll
-                        for (int r = 0; r < RW; ++r)
-#pragma unroll
-                            for (int j = 0; j < NR; ++j) {
-                                acc[r][j] = fmaf(a[u][r].x, b[j].x, acc[r][j]);
-                                acc[r][j] = fmaf(a[u][r].y, b[j].y, acc[r][j]);
-                                acc[r][j] = fmaf(a[u][r].z, b[j].z, acc[r][j]);
-                                acc[r][j] = fmaf(a[u][r].w, b[j].w, acc[r][j]);
-                            }
-                    }
-                }
-            }
-            for (; k < kend; k += 256) {
+            for (int k = k0 + 4 * lane; k < kend; k += 256) {
                 f32x4 a[RW];
                 if (k + 3 < K) {
 #pragma unroll
@@ -298,20 +272,20 @@ static hipError_t launch_cols_u(const ColStream &q, hipStream_t s) {
                   q.cols, q.K, q.X, q.ldx, q.y, q.yk, q.yj, q.out, q.ci, q.cj, q.alpha, q.beta);
 }
 
-// Steps per batch.  With y read along k (YM 2), two dense columns (YM 4) or y
-// gathered into LDS (YM 5), two rows per wave and at most four columns: eight
-// steps of 256 k per batch when K >= 2048 (four with four columns, or when a
-// chunk of y holds only four), four when K is shorter, one step at a time
+// Steps per batch.  With y read along k (YM 2) or two dense columns (YM 4), two
+// rows per wave and at most four columns: eight steps of 256 k per batch when K
+// >= 2048 (four with four columns), four when K is shorter, one step at a time
 // otherwise.  Against one step at a time (back-to-back launches, the same box):
 // 4096 x 1 x 4096 11.9 -> 11.4 us, 2048 x 1 x 16384 30.7 -> 25.0 us, a row times
 // a transposed 4096 x 4096 matrix streamed from HBM 14.9 -> 13.9 us, 4096 x 2 x
-// 4096 and the last column of 4095 x 4097 x 1023 level.  The other modes load
-// more values of y per step and keep one step at a time.
+// 4096 level.  With y gathered into LDS (YM 5) four steps per batch made the
+// last column of 4095 x 4097 x 1023 slower (6.35 -> 6.84 us traced), and the
+// modes that read whole rows of y lost as well; they take one step at a time.
 template <int NR, int RW, int YM>
 static hipError_t launch_cols(const ColStream &q, hipStream_t s) {
-    constexpr bool BATCH = RW == 2 && (YM == 2 || YM == 4 || YM == 5) && NR <= 4;
+    constexpr bool BATCH = RW == 2 && (YM == 2 || YM == 4) && NR <= 4;
     if constexpr (BATCH) {
-        constexpr int UMAX = NR == 4 ? 4 : YM == 5 ? skinny_n_chunk<NR>() / 256 : 8;
+        constexpr int UMAX = NR == 4 ? 4 : 8;
         if (UMAX >= 8 && q.K >= 2048) return launch_cols_u<NR, RW, YM, (UMAX >= 8 ? 8 : 1)>(q, s);
         if (q.K > 768) return launch_cols_u<NR, RW, YM, 4>(q, s);  // four steps per lane
     }
