@@ -233,6 +233,27 @@ def test_ragged_large_sampled(layout):
     check_ex(As, Bs, M, N, K, ta, tb, 1.0, 1.0, C0, C, f"ragged {lid(layout)}", rows=r, cols=c)
 
 
+@pytest.mark.parametrize("layout", [(N_, T_), (T_, N_), (T_, T_)], ids=lid)
+@pytest.mark.parametrize("shape", [(2048, 3072, 4096), (8192, 8192, 8192)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_headline_workloads_transposed_sampled(shape, layout):
+    """2048 x 3072 x 4096 and 8192^3 with transposed operands, as bench.py --layout
+    times them: N(0,1) within the tolerance, and for the smaller one small integers
+    bitwise, on sampled rows, columns and elements."""
+    from gpu_helpers import sample_indices
+    ta, tb = layout
+    M, N, K = shape
+    As, Bs, C0 = _operands(M, N, K, "normal", 3 if M == 2048 else 6, ta, tb)
+    C = _run(As, Bs, M, N, K, ta, tb, 1.0, 0.0, C0)
+    r, c = sample_indices(M, N, rows=4, cols=4, elems=2048, seed=13)
+    check_ex(As, Bs, M, N, K, ta, tb, 1.0, 0.0, C0, C, f"{shape} {lid(layout)}", rows=r, cols=c)
+    if M == 2048:
+        As, Bs, C0 = _operands(M, N, K, "smallint", 33, ta, tb)
+        C = _run(As, Bs, M, N, K, ta, tb, 2.0, -1.0, C0)
+        check_ex(As, Bs, M, N, K, ta, tb, 2.0, -1.0, C0, C, f"{shape} {lid(layout)} int",
+                 exact=True, rows=r, cols=c)
+
+
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lid)
 def test_colmajor_entry(layout):
     """Column-major arrays, reference-BLAS argument order: the same product as the
